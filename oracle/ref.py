@@ -1,0 +1,320 @@
+"""CPU oracle for one rank's share of a Ulysses attention layer (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP library and never imports it; the library never falls back to it.
+
+Every function is the plain definition of what the step computes, written
+out in float64 with no blocking beyond what is stated:
+
+* relayout - index arithmetic of the all-to-all that swaps sequence sharding
+  for head sharding (Transformers guide "Ulysses sequence parallelism",
+  introduction and its two-GPU figure; blog "Ulysses Sequence Parallelism:
+  Training with Million-Token Contexts", "How Ulysses works", steps 1, 3, 5).
+* mask - causal attention within each packed sample, with sample boundaries
+  read from position_ids rather than a 4D mask (Transformers guide,
+  "Configuration", the sp_attn_implementation item; Accelerate guide
+  "Sequence parallelism in accelerate", "ALST/Ulysses SP backend
+  configuration", the sp_attn_implementation item; blog, "Loss aggregation"
+  paragraph on position_ids).
+* attention forward/backward - standard softmax attention for each local
+  head (blog, "How Ulysses works", step 4; heads independent, same section).
+* weighted loss - the token-weighted aggregation of per-rank losses
+  (Accelerate guide, "ALST/Ulysses SP backend configuration", the loss
+  aggregation loop; blog, "Loss aggregation").
+
+Readings taken where the pages are silent (the pages give no formulas for
+these): a sample starts at index 0 and wherever position_ids is 0; causality
+is by sequence index within a sample; softmax scale defaults to 1/sqrt(d);
+LSE uses the natural log; query head h uses KV head h // (hq/hkv); rank r
+holds tokens [r*N/P, (r+1)*N/P) and heads [r*H/P, (r+1)*H/P); a rank's loss is
+the mean over its valid tokens.
+
+Parity pins: see tests/test_oracle.py (brute force, closed forms,
+invariants, finite differences).  Every function here is pinned there.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+IGNORE_INDEX = -100
+
+
+# ---------------------------------------------------------------------------
+# bf16 <-> float64
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening: put the 16 bits in the top half of a float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Relayout: the all-to-all as a permutation of bits
+# ---------------------------------------------------------------------------
+
+def seq_to_head(x_seq: np.ndarray, rank: int = -1) -> np.ndarray:
+    """Sequence-sharded [P][N/P][G][H][d] -> head-sharded layout.
+
+    Rank p holds tokens [p*N/P, (p+1)*N/P) for all H heads; after the
+    exchange rank q holds all N tokens for heads [q*H/P, (q+1)*H/P):
+        out[q][g][p*N/P + t][hl][e] = x_seq[p][t][g][q*H/P + hl][e]
+    rank == -1 returns all ranks, [P][G][N][H/P][d]; rank == r returns rank
+    r's share, [G][N][H/P][d].  Bits are moved verbatim.
+    """
+    P, T, G, H, d = x_seq.shape
+    if H % P:
+        raise ValueError("heads not divisible by sp_size")
+    hl = H // P
+    v = x_seq.reshape(P, T, G, P, hl, d)          # [p][t][g][q][hl][e]
+    out = v.transpose(3, 2, 0, 1, 4, 5)           # [q][g][p][t][hl][e]
+    out = np.ascontiguousarray(out).reshape(P, G, P * T, hl, d)
+    return out if rank < 0 else np.ascontiguousarray(out[rank])
+
+
+def head_to_seq(x_head: np.ndarray, sp_size: int, rank: int = -1,
+                out: np.ndarray | None = None) -> np.ndarray:
+    """Inverse of seq_to_head.  rank == r takes rank r's share [G][N][H/P][d]
+    and writes only head columns [r*H/P, (r+1)*H/P) of ``out`` (created as
+    zeros if not given)."""
+    P = sp_size
+    if rank < 0:
+        _, G, N, hl, d = x_head.shape
+        T = N // P
+        v = x_head.reshape(P, G, P, T, hl, d)     # [q][g][p][t][hl][e]
+        return np.ascontiguousarray(v.transpose(2, 3, 1, 0, 4, 5)).reshape(P, T, G, P * hl, d)
+    G, N, hl, d = x_head.shape
+    T = N // P
+    if out is None:
+        out = np.zeros((P, T, G, P * hl, d), dtype=x_head.dtype)
+    v = x_head.reshape(G, P, T, hl, d)            # [g][p][t][hl][e]
+    out[:, :, :, rank * hl:(rank + 1) * hl, :] = v.transpose(1, 2, 0, 3, 4)
+    return out
+
+
+def gather_share(x_seq: np.ndarray, rank: int, g0: int = 0, g1: int | None = None) -> np.ndarray:
+    """Rank ``rank``'s head block of groups [g0, g1) as a token-major
+    [N][G'][H/P][d] array (the layout attention consumes)."""
+    P, T, G, H, d = x_seq.shape
+    g1 = G if g1 is None else g1
+    hl = H // P
+    s = x_seq[:, :, g0:g1, rank * hl:(rank + 1) * hl, :]
+    return np.ascontiguousarray(s).reshape(P * T, g1 - g0, hl, d)
+
+
+# ---------------------------------------------------------------------------
+# Segments and the mask
+# ---------------------------------------------------------------------------
+
+def segment_ids(position_ids: np.ndarray) -> np.ndarray:
+    """A new sample starts at token 0 and at every token whose position_id is 0."""
+    pos = np.asarray(position_ids)
+    start = (pos == 0)
+    if start.size:
+        start[0] = True
+    return np.cumsum(start) - 1
+
+
+def segment_first(position_ids: np.ndarray) -> np.ndarray:
+    """Index of the first token of each token's sample (from the segment ids)."""
+    seg = segment_ids(position_ids)
+    n = seg.size
+    firsts = np.flatnonzero(np.r_[True, seg[1:] != seg[:-1]]) if n else np.zeros(0, np.int64)
+    return firsts[seg] if n else np.zeros(0, np.int64)
+
+
+def allowed(seg: np.ndarray, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
+    """Explicit boolean mask block: query i may see key j iff they lie in the
+    same sample and j <= i."""
+    rows = np.asarray(rows)[:, None]
+    cols = np.asarray(cols)[None, :]
+    return (seg[rows] == seg[cols]) & (cols <= rows)
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _as_f64(x):
+    x = np.asarray(x)
+    return bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
+def _scale(d, softmax_scale):
+    return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+
+def _row_blocks(n, seg, first, block_rows):
+    """Yield (rows, cols): a block of consecutive query rows and the key span
+    [first token of the block's first sample, last row].  Keys outside it are
+    masked for every row of the block, so they contribute exact zeros."""
+    for r0 in range(0, n, block_rows):
+        r1 = min(n, r0 + block_rows)
+        c0 = int(first[r0])
+        yield np.arange(r0, r1), np.arange(c0, r1)
+
+
+def _probs(qh, kh, seg, rows, cols, scale):
+    """Row softmax of scale*q k^T over the explicit mask: returns P, m, l."""
+    S = scale * (qh[rows] @ kh[cols].T)
+    S[~allowed(seg, rows, cols)] = -np.inf
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return E / l, m[:, 0], l[:, 0]
+
+
+def attn_fwd(q, k, v, position_ids, softmax_scale=None, block_rows=256):
+    """O = softmax(scale q k^T + mask) v and LSE = log sum exp(scale q k) over
+    allowed keys, per local query head.
+
+    q: [N][hq][d], k, v: [N][hkv][d] (bf16 bits or floats).  Returns
+    o [N][hq][d] and lse [hq][N], float64."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    scale = _scale(d, softmax_scale)
+    seg = segment_ids(position_ids)
+    first = segment_first(position_ids)
+    o = np.zeros((N, hq, d))
+    lse = np.zeros((hq, N))
+    for h in range(hq):
+        kv = h // grp
+        qh, kh, vh = q[:, h], k[:, kv], v[:, kv]
+        for rows, cols in _row_blocks(N, seg, first, block_rows):
+            P, m, l = _probs(qh, kh, seg, rows, cols, scale)
+            o[rows, h] = P @ vh[cols]
+            lse[h, rows] = m + np.log(l)
+    return o, lse
+
+
+def attn_bwd(q, k, v, do, position_ids, softmax_scale=None, block_rows=256):
+    """Gradients of sum(dO * O) with respect to q, k, v (float64).
+
+    With P the attention probabilities: dV = P^T dO, dP = dO v^T,
+    D_i = sum_j P_ij dP_ij, dS = P * (dP - D), dQ = scale dS k,
+    dK = scale dS^T q; dK/dV of a KV head sum over the query heads that
+    share it."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    scale = _scale(d, softmax_scale)
+    seg = segment_ids(position_ids)
+    first = segment_first(position_ids)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(hq):
+        kv = h // grp
+        qh, kh, vh, doh = q[:, h], k[:, kv], v[:, kv], do[:, h]
+        for rows, cols in _row_blocks(N, seg, first, block_rows):
+            P, _, _ = _probs(qh, kh, seg, rows, cols, scale)
+            dv[cols, kv] += P.T @ doh[rows]
+            dP = doh[rows] @ vh[cols].T
+            D = (P * dP).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dq[rows, h] = scale * (dS @ kh[cols])
+            dk[cols, kv] += scale * (dS.T @ qh[rows])
+    return dq, dk, dv
+
+
+def attn_rows(q, k, v, do, position_ids, rows, softmax_scale=None, chunk=64):
+    """O, LSE and dQ for selected query rows only (each row's full softmax
+    over all its allowed keys).  Returns o [R][hq][d], lse [hq][R],
+    dq [R][hq][d] (dq is None when do is None)."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    do = None if do is None else _as_f64(do)
+    N, hq, d = q.shape
+    grp = hq // k.shape[1]
+    scale = _scale(d, softmax_scale)
+    seg = segment_ids(position_ids)
+    first = segment_first(position_ids)
+    rows = np.asarray(rows, dtype=np.int64)
+    R = rows.size
+    o = np.zeros((R, hq, d))
+    lse = np.zeros((hq, R))
+    dq = None if do is None else np.zeros((R, hq, d))
+    for c0 in range(0, R, chunk):
+        sel = np.arange(c0, min(R, c0 + chunk))
+        rr = rows[sel]
+        cols = np.arange(int(first[rr].min()), int(rr.max()) + 1)
+        for h in range(hq):
+            kv = h // grp
+            P, m, l = _probs(q[:, h], k[:, kv], seg, rr, cols, scale)
+            o[sel, h] = P @ v[cols, kv]
+            lse[h, sel] = m + np.log(l)
+            if do is not None:
+                dP = do[rr, h] @ v[cols, kv].T
+                D = (P * dP).sum(axis=1, keepdims=True)
+                dq[sel, h] = scale * ((P * (dP - D)) @ k[cols, kv])
+    return o, lse, dq
+
+
+def attn_key_cols(q, k, v, do, position_ids, cols, softmax_scale=None):
+    """dK and dV for selected key columns only.  Key j receives gradient from
+    the query rows i >= j of its own sample; every such row's full softmax
+    (over all its allowed keys) is recomputed.  Returns dk, dv [C][hkv][d]."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    scale = _scale(d, softmax_scale)
+    seg = segment_ids(position_ids)
+    first = segment_first(position_ids)
+    cols = np.asarray(cols, dtype=np.int64)
+    dk = np.zeros((cols.size, hkv, d))
+    dv = np.zeros((cols.size, hkv, d))
+    for s in np.unique(seg[cols]):
+        sel = np.flatnonzero(seg[cols] == s)
+        cc = cols[sel]
+        last = int(np.flatnonzero(seg == s)[-1])
+        rows = np.arange(int(cc.min()), last + 1)       # rows that can see any of cc
+        span = np.arange(int(first[rows[0]]), last + 1)  # all keys those rows see
+        for h in range(hq):
+            kv = h // grp
+            for r0 in range(0, rows.size, 128):
+                rr = rows[r0:r0 + 128]
+                P, _, _ = _probs(q[:, h], k[:, kv], seg, rr, span, scale)
+                dP = do[rr, h] @ v[span, kv].T
+                D = (P * dP).sum(axis=1, keepdims=True)
+                dS = P * (dP - D)
+                pos_c = cc - span[0]
+                dv[sel, kv] += P[:, pos_c].T @ do[rr, h]
+                dk[sel, kv] += scale * (dS[:, pos_c].T @ q[rr, h])
+    return dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Token-weighted loss across ranks
+# ---------------------------------------------------------------------------
+
+def weighted_loss(token_loss, shift_labels, ignore_index=IGNORE_INDEX):
+    """Token-weighted mean of per-rank losses, following the pages' loop:
+    good_r = #valid tokens of rank r; rank r's loss = mean of its valid token
+    losses (NaN if it has none); total = sum over ranks with good_r > 0 of
+    loss_r * good_r; loss = total / max(sum_r good_r, 1).
+
+    Returns loss, rank_loss [P], good [P] (int64) and d loss / d token_loss
+    [P][N/P] (1/max(T,1) on valid tokens, 0 elsewhere).  float64."""
+    tl = np.asarray(token_loss, dtype=np.float64)
+    lab = np.asarray(shift_labels)
+    P = tl.shape[0]
+    valid = lab != ignore_index
+    good = valid.sum(axis=1).astype(np.int64)
+    rank_loss = np.full(P, np.nan)
+    for r in range(P):
+        if good[r] > 0:
+            rank_loss[r] = tl[r][valid[r]].sum() / good[r]
+    total = 0.0
+    for r in range(P):
+        if good[r] > 0:                      # a rank with no valid tokens is skipped: NaN*0 = NaN
+            total = total + rank_loss[r] * good[r]
+    T = int(good.sum())
+    loss = total / max(T, 1)
+    dtl = np.where(valid, 1.0 / max(T, 1), 0.0)
+    return float(loss), rank_loss, good, dtl

@@ -1,0 +1,466 @@
+"""Pins for the CPU oracle: brute force on tiny inputs, closed forms, invariants,
+finite differences and the pages' own statements.  CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import ref
+from synth import configs, gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(seed, shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _read_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ---------------------------------------------------------------------------
+# Relayout
+# ---------------------------------------------------------------------------
+
+def _tagged(P, T, G, H, d):
+    """Each element's value encodes (p, t, g, h, e) so its destination can be read back."""
+    p, t, g, h, e = np.meshgrid(np.arange(P), np.arange(T), np.arange(G), np.arange(H),
+                                np.arange(d), indexing="ij")
+    return (((((p * T + t) * G + g) * H + h) * d) + e).astype(np.int64), (p * T + t), g, h, e
+
+
+def test_two_gpu_figure_layouts():
+    """The figure: GPU i first holds tokens [i N/2, (i+1) N/2) for all heads; after the
+    exchange it holds all N tokens for heads [i H/2, (i+1) H/2); the second exchange
+    returns the first layout."""
+    P, T, G, H, d = 2, 5, 1, 6, 3
+    N = P * T
+    x, tok, grp, head, e = _tagged(P, T, G, H, d)
+    sym = {"0": 0, "N/2": N // 2, "N": N, "H/2": H // 2, "H": H}
+    rows = _read_golden("two_gpu_figure.txt")
+    h2 = ref.seq_to_head(x)
+    back = ref.head_to_seq(h2, P)
+    for phase, gpu, trange, hrange in rows:
+        gpu = int(gpu)
+        t0, t1 = (sym[s] for s in trange.split(":"))
+        h0, h1 = (sym[s] for s in hrange.split(":"))
+        if phase in ("seq_sharded", "back_to_seq"):
+            arr = x if phase == "seq_sharded" else back
+            held_tok = tok[gpu] if phase == "seq_sharded" else tok[gpu]
+            assert np.array_equal(arr[gpu], x[gpu])
+            assert held_tok.min() == t0 and held_tok.max() == t1 - 1
+        else:
+            share = h2[gpu]                        # [G][N][H/P][d]
+            n_idx = np.arange(N)[None, :, None, None]
+            hl = np.arange(H // P)[None, None, :, None]
+            ee = np.arange(d)[None, None, None, :]
+            gg = np.arange(G)[:, None, None, None]
+            # decode each element back into (token, head) and check the ranges
+            dec_e = share % d
+            dec_h = (share // d) % H
+            dec_g = (share // (d * H)) % G
+            dec_tok = share // (d * H * G)
+            assert np.array_equal(dec_e, np.broadcast_to(ee, share.shape))
+            assert np.array_equal(dec_g, np.broadcast_to(gg, share.shape))
+            assert np.array_equal(dec_tok, np.broadcast_to(n_idx, share.shape))
+            assert np.array_equal(dec_h, np.broadcast_to(h0 + hl, share.shape))
+            assert dec_tok.min() == t0 and dec_tok.max() == t1 - 1
+            assert dec_h.min() == h0 and dec_h.max() == h1 - 1
+
+
+@pytest.mark.parametrize("P,T,G,H,d", [(1, 4, 3, 2, 2), (2, 3, 1, 4, 2), (3, 2, 2, 6, 4),
+                                       (4, 3, 3, 8, 2), (8, 2, 2, 16, 1)])
+def test_relayout_places_every_element(P, T, G, H, d):
+    """After seq->head, rank q holds global token p*T+t, group g, head q*H/P+hl at
+    [q][g][p*T+t][hl]; every source element appears exactly once."""
+    x, tok, grp, head, e = _tagged(P, T, G, H, d)
+    out = ref.seq_to_head(x)
+    hl = H // P
+    assert out.shape == (P, G, P * T, hl, d)
+    for q in range(P):
+        for g in range(G):
+            for n in range(P * T):
+                for j in range(hl):
+                    expect = (((n * G + g) * H + q * hl + j) * d) + np.arange(d)
+                    assert np.array_equal(out[q, g, n, j], expect)
+    assert np.array_equal(np.sort(out.ravel()), np.sort(x.ravel()))
+
+
+def test_relayout_p1_is_textbook_transpose():
+    x = gen.raw_bits_u16((99, 1), (1, 7, 3, 5, 4))
+    out = ref.seq_to_head(x)
+    assert np.array_equal(out[0], np.transpose(x[0], (1, 0, 2, 3)))
+
+
+@pytest.mark.parametrize("P,T,G,H,d", [(2, 3, 3, 4, 8), (4, 5, 1, 8, 16), (8, 2, 2, 8, 8)])
+def test_relayout_roundtrip_and_rank_slices_bitexact(P, T, G, H, d):
+    x = gen.raw_bits_u16((99, P), (P, T, G, H, d))   # includes NaN payloads, -0, subnormals
+    h = ref.seq_to_head(x)
+    assert np.array_equal(ref.head_to_seq(h, P), x)
+    y = np.zeros_like(x)
+    for r in range(P):
+        s = ref.seq_to_head(x, rank=r)
+        assert np.array_equal(s, h[r])
+        ref.head_to_seq(s, P, rank=r, out=y)
+    assert np.array_equal(y, x)
+    # a single rank's write touches only its own head columns
+    z = np.zeros_like(x)
+    ref.head_to_seq(h[1 % P], P, rank=1 % P, out=z)
+    hl = H // P
+    mask = np.zeros(H, bool)
+    mask[(1 % P) * hl:((1 % P) + 1) * hl] = True
+    assert np.array_equal(z[..., mask, :], x[..., mask, :])
+    assert not z[..., ~mask, :].any()
+
+
+def test_head_divisibility_golden():
+    for H_s, *accepted in _read_golden("head_divisibility.txt"):
+        H = int(H_s.rstrip(":"))
+        acc = {int(a) for a in accepted}
+        for P in range(1, H + 1):
+            x = np.zeros((P, 1, 1, H, 1), np.uint16)
+            if P in acc:
+                ref.seq_to_head(x)
+            else:
+                with pytest.raises(ValueError):
+                    ref.seq_to_head(x)
+
+
+# ---------------------------------------------------------------------------
+# Mask
+# ---------------------------------------------------------------------------
+
+def _brute_allowed(pos):
+    """Query i sees key j iff j <= i and no sample starts in (j, i]."""
+    n = len(pos)
+    out = np.zeros((n, n), bool)
+    for i in range(n):
+        for j in range(i + 1):
+            ok = True
+            for s in range(j + 1, i + 1):
+                if pos[s] == 0:
+                    ok = False
+                    break
+            out[i, j] = ok
+    return out
+
+
+@pytest.mark.parametrize("pos", [
+    list(range(10)),
+    [0, 1, 2, 0, 1, 0, 0, 1, 2, 3, 4],
+    [0] * 7,
+    [5, 6, 7, 0, 1, 2, 3],          # first token always starts a sample
+    [0, 1, 2, 3, 0, 1],             # truncated last sample
+    [0, 2, 9, 0, 3, 1, 0],          # non-consecutive positions: only zeros start samples
+])
+def test_mask_brute_force(pos):
+    pos = np.array(pos, np.int64)
+    seg = ref.segment_ids(pos)
+    n = len(pos)
+    got = ref.allowed(seg, np.arange(n), np.arange(n))
+    assert np.array_equal(got, _brute_allowed(pos))
+    first = ref.segment_first(pos)
+    for i in range(n):
+        assert first[i] == min(j for j in range(n) if _brute_allowed(pos)[i, j])
+
+
+# ---------------------------------------------------------------------------
+# Attention forward
+# ---------------------------------------------------------------------------
+
+def _brute_fwd(q, k, v, pos, scale):
+    """Pure-Python loops: per head and row, softmax over keys allowed by the brute mask."""
+    N, hq, d = q.shape
+    grp = hq // k.shape[1]
+    A = _brute_allowed(pos)
+    o = np.zeros_like(q)
+    lse = np.zeros((hq, N))
+    for h in range(hq):
+        kv = h // grp
+        for i in range(N):
+            s = {}
+            for j in range(N):
+                if A[i, j]:
+                    s[j] = scale * sum(q[i, h, e] * k[j, kv, e] for e in range(d))
+            m = max(s.values())
+            w = {j: math.exp(x - m) for j, x in s.items()}
+            tot = sum(w.values())
+            for e in range(d):
+                o[i, h, e] = sum(w[j] * v[j, kv, e] for j in w) / tot
+            lse[h, i] = m + math.log(tot)
+    return o, lse
+
+
+@pytest.mark.parametrize("N,hq,hkv,d,pos_kind", [(24, 2, 1, 4, "packed"), (17, 3, 3, 8, "single"),
+                                                 (32, 4, 2, 5, "packed")])
+def test_fwd_brute_force(N, hq, hkv, d, pos_kind):
+    q, k, v = _rand(1, (N, hq, d)), _rand(2, (N, hkv, d)), _rand(3, (N, hkv, d))
+    if pos_kind == "packed":
+        pos = gen.position_ids_from_lengths([5, 1, 9, N - 15])
+    else:
+        pos = np.arange(N)
+    scale = 0.37
+    o, lse = ref.attn_fwd(q, k, v, pos, softmax_scale=scale, block_rows=5)
+    ob, lb = _brute_fwd(q, k, v, pos, scale)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=1e-12, atol=1e-13)
+
+
+def test_fwd_rows_sum_to_one_and_default_scale():
+    N, hq, hkv, d = 40, 4, 2, 16
+    q, k = _rand(4, (N, hq, d)), _rand(5, (N, hkv, d))
+    pos = gen.position_ids_from_lengths([13, 20, 7])
+    o, _ = ref.attn_fwd(q, k, np.ones((N, hkv, d)), pos)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-13)
+    # default scale is 1/sqrt(d)
+    v = _rand(6, (N, hkv, d))
+    a, la = ref.attn_fwd(q, k, v, pos)
+    b, lb = ref.attn_fwd(q, k, v, pos, softmax_scale=1 / math.sqrt(d))
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_fwd_zero_scale_is_uniform_mean():
+    """scale 0: every allowed key weighs the same, O_i is the mean of V over [start, i]."""
+    N, d = 23, 3
+    q, k, v = _rand(7, (N, 1, d)), _rand(8, (N, 1, d)), _rand(9, (N, 1, d))
+    pos = gen.position_ids_from_lengths([4, 11, 8])
+    o, lse = ref.attn_fwd(q, k, v, pos, softmax_scale=0.0)
+    first = [0] * 4 + [4] * 11 + [15] * 8
+    for i in range(N):
+        np.testing.assert_allclose(o[i, 0], v[first[i]:i + 1, 0].mean(axis=0), rtol=1e-12)
+        assert abs(lse[0, i] - math.log(i - first[i] + 1)) < 1e-12
+
+
+def test_fwd_segment_start_rows_and_all_zero_positions():
+    N, hq, hkv, d = 30, 4, 2, 8
+    q, k, v = _rand(10, (N, hq, d)), _rand(11, (N, hkv, d)), _rand(12, (N, hkv, d))
+    lens = [6, 1, 10, 13]
+    pos = gen.position_ids_from_lengths(lens)
+    scale = 0.5
+    o, lse = ref.attn_fwd(q, k, v, pos, softmax_scale=scale)
+    starts = np.cumsum([0] + lens[:-1])
+    for i in starts:
+        for h in range(hq):
+            kv = h // 2
+            assert np.array_equal(o[i, h], v[i, kv])
+            assert abs(lse[h, i] - scale * np.dot(q[i, h], k[i, kv])) < 1e-12
+    o0, _ = ref.attn_fwd(q, k, v, np.zeros(N, np.int64))
+    for h in range(hq):
+        assert np.array_equal(o0[:, h], v[:, h // 2])
+
+
+def test_fwd_constant_key_is_cumulative_mean():
+    N, d = 26, 4
+    q = _rand(13, (N, 2, d))
+    k = np.tile(_rand(14, (1, 1, d)), (N, 1, 1))
+    v = _rand(15, (N, 1, d))
+    pos = gen.position_ids_from_lengths([9, 17])
+    o, lse = ref.attn_fwd(q, k, v, pos, softmax_scale=0.3)
+    for i in range(N):
+        s = 0 if i < 9 else 9
+        for h in range(2):
+            np.testing.assert_allclose(o[i, h], v[s:i + 1, 0].mean(axis=0), rtol=1e-12)
+            expect = 0.3 * np.dot(q[i, h], k[0, 0]) + math.log(i - s + 1)
+            assert abs(lse[h, i] - expect) < 1e-12
+
+
+def test_fwd_packed_equals_separate_and_chunking():
+    lens = [37, 5, 64, 1, 50]
+    N, hq, hkv, d = sum(lens), 4, 1, 16
+    q, k, v = _rand(16, (N, hq, d)), _rand(17, (N, hkv, d)), _rand(18, (N, hkv, d))
+    pos = gen.position_ids_from_lengths(lens)
+    o, lse = ref.attn_fwd(q, k, v, pos, block_rows=16)
+    o_full, lse_full = ref.attn_fwd(q, k, v, pos, block_rows=N)
+    np.testing.assert_allclose(o, o_full, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_full, rtol=1e-12, atol=1e-14)
+    s = 0
+    for L in lens:
+        sl = slice(s, s + L)
+        os_, ls_ = ref.attn_fwd(q[sl], k[sl], v[sl], np.arange(L), block_rows=7)
+        np.testing.assert_allclose(o[sl], os_, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse[:, sl], ls_, rtol=1e-12, atol=1e-14)
+        s += L
+    # a boundary-blind mask (one sample) must differ: the SDPA failure mode on packed rows
+    o_blind, _ = ref.attn_fwd(q, k, v, np.arange(N))
+    assert np.abs(o_blind[37:] - o[37:]).max() > 1e-3
+
+
+def test_full_layer_sp_equivalence():
+    """seq->head, attention on each rank's heads, head->seq == attention over all heads
+    on the unsharded sequence (heads are independent)."""
+    P, T, H, d = 4, 8, 8, 8
+    N = P * T
+    qkv = gen.normal_bf16((77, 1), (P, T, 3, H, d))
+    pos = gen.position_ids_from_lengths([11, 21])
+    h2 = ref.seq_to_head(qkv)                       # [P][3][N][H/P][d]
+    outs = []
+    for r in range(P):
+        o, _ = ref.attn_fwd(h2[r, 0], h2[r, 1], h2[r, 2], pos)
+        outs.append(o)
+    # head->seq of the float outputs: reuse the permutation on float arrays
+    o_head = np.stack(outs)[:, None]                # [P][1][N][H/P][d]
+    o_seq = ref.head_to_seq(o_head, P)              # [P][T][1][H][d]
+    full = qkv.reshape(N, 3, H, d)
+    o_ref, _ = ref.attn_fwd(full[:, 0], full[:, 1], full[:, 2], pos)
+    np.testing.assert_allclose(o_seq.reshape(N, H, d), o_ref, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Attention backward
+# ---------------------------------------------------------------------------
+
+def test_bwd_finite_differences():
+    N, hq, hkv, d = 14, 4, 2, 3
+    q, k, v, do = _rand(20, (N, hq, d)), _rand(21, (N, hkv, d)), _rand(22, (N, hkv, d)), _rand(23, (N, hq, d))
+    pos = gen.position_ids_from_lengths([6, 1, 7])
+    scale = 0.8
+    dq, dk, dv = ref.attn_bwd(q, k, v, do, pos, softmax_scale=scale, block_rows=4)
+
+    def f(q_, k_, v_):
+        o, _ = ref.attn_fwd(q_, k_, v_, pos, softmax_scale=scale)
+        return float((o * do).sum())
+
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (f(**{kk + "_": vv for kk, vv in args_p.items()})
+                        - f(**{kk + "_": vv for kk, vv in args_m.items()})) / (2 * eps)
+        err = np.abs(num - g).max() / np.abs(g).max()
+        assert err < 1e-7, (name, err)
+
+
+def test_bwd_gqa_equals_replicated_sum():
+    N, hq, hkv, d = 33, 6, 2, 8
+    grp = hq // hkv
+    q, k, v, do = _rand(24, (N, hq, d)), _rand(25, (N, hkv, d)), _rand(26, (N, hkv, d)), _rand(27, (N, hq, d))
+    pos = gen.position_ids_from_lengths([20, 13])
+    dq, dk, dv = ref.attn_bwd(q, k, v, do, pos)
+    kr, vr = np.repeat(k, grp, axis=1), np.repeat(v, grp, axis=1)
+    dq2, dk2, dv2 = ref.attn_bwd(q, kr, vr, do, pos)
+    np.testing.assert_allclose(dq, dq2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk, dk2.reshape(N, hkv, grp, d).sum(2), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(N, hkv, grp, d).sum(2), rtol=1e-11, atol=1e-13)
+
+
+def test_bwd_special_cases_and_segment_sums():
+    N, hq, hkv, d = 40, 4, 1, 8
+    q, k, v, do = _rand(28, (N, hq, d)), _rand(29, (N, hkv, d)), _rand(30, (N, hkv, d)), _rand(31, (N, hq, d))
+    lens = [12, 1, 27]
+    pos = gen.position_ids_from_lengths(lens)
+    dq, dk, dv = ref.attn_bwd(q, k, v, do, pos, block_rows=9)
+    starts = np.cumsum([0] + lens[:-1])
+    assert not dq[starts].any()                          # a sample's first row sees only itself
+    s = 0
+    for L in lens:                                       # per sample: sum_j dV_j = sum_i dO_i, sum_j dK_j = 0
+        np.testing.assert_allclose(dv[s:s + L, 0].sum(0), do[s:s + L].sum((0, 1)), rtol=1e-11, atol=1e-12)
+        assert np.abs(dk[s:s + L, 0].sum(0)).max() < 1e-12
+        s += L
+    z = np.zeros(N, np.int64)
+    dq0, dk0, dv0 = ref.attn_bwd(q, k, v, do, z)
+    assert not dq0.any() and not dk0.any()
+    np.testing.assert_allclose(dv0[:, 0], do.sum(1), rtol=1e-13)
+
+
+def test_sampled_rows_and_cols_match_full():
+    lens = [70, 3, 100, 37]
+    N, hq, hkv, d = sum(lens), 4, 2, 16
+    q, k, v, do = (gen.normal_bf16((55, s), sh) for s, sh in
+                   ((1, (N, hq, d)), (2, (N, hkv, d)), (3, (N, hkv, d)), (4, (N, hq, d))))
+    pos = gen.position_ids_from_lengths(lens)
+    o, lse = ref.attn_fwd(q, k, v, pos, block_rows=32)
+    dq, dk, dv = ref.attn_bwd(q, k, v, do, pos, block_rows=32)
+    rows = np.array([0, 1, 69, 70, 71, 72, 73, 100, 172, 173, 200, N - 1])
+    o_s, lse_s, dq_s = ref.attn_rows(q, k, v, do, pos, rows, chunk=5)
+    np.testing.assert_allclose(o_s, o[rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse_s, lse[:, rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dq_s, dq[rows], rtol=1e-11, atol=1e-12)
+    cols = np.array([0, 5, 69, 70, 72, 73, 150, 172, 173, 190, N - 1])
+    dk_s, dv_s = ref.attn_key_cols(q, k, v, do, pos, cols)
+    np.testing.assert_allclose(dk_s, dk[cols], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv_s, dv[cols], rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Token-weighted loss
+# ---------------------------------------------------------------------------
+
+def test_loss_worked_example_prompt_only_rank():
+    """Rank 0 holds only prompt tokens (all -100); rank 1 has 3 valid tokens with losses
+    1, 2, 3: rank losses (NaN, 2), total 2*3 = 6 over 3 tokens -> 2.0."""
+    tl = np.array([[9.0, 9.0, 9.0, 9.0], [1.0, 100.0, 2.0, 3.0]])
+    lab = np.array([[-100] * 4, [5, -100, 7, 8]])
+    loss, rl, good, dtl = ref.weighted_loss(tl, lab)
+    assert loss == 2.0
+    assert np.isnan(rl[0]) and rl[1] == 2.0
+    assert list(good) == [0, 3]
+    assert np.array_equal(dtl, np.array([[0, 0, 0, 0], [1 / 3, 0, 1 / 3, 1 / 3]]))
+
+
+@pytest.mark.parametrize("P", [1, 2, 8])
+def test_loss_closed_form(P):
+    rng = np.random.default_rng(P)
+    tl = rng.uniform(0, 12, (P, 64))
+    lab = rng.integers(0, 1000, (P, 64))
+    lab[rng.random((P, 64)) < 0.3] = -100
+    loss, rl, good, dtl = ref.weighted_loss(tl, lab)
+    valid = lab != -100
+    T = valid.sum()
+    assert abs(loss - tl[valid].sum() / T) < 1e-12 * abs(loss)
+    # P == 1 reduces to the plain masked mean; per-rank loss is that rank's masked mean
+    for r in range(P):
+        assert abs(rl[r] - tl[r][valid[r]].mean()) < 1e-12
+    np.testing.assert_array_equal(dtl, np.where(valid, 1.0 / T, 0.0))
+
+
+def test_loss_zero_rank_and_all_masked():
+    w = configs.Workload(3, "t", 8, 1024, 1, 1, 8, prompt_frac=0.15)
+    inp = configs.loss_inputs(w)
+    lab = inp["shift_labels"].copy()
+    lab[0] = -100                                   # rank 0 fully masked
+    loss, rl, good, dtl = ref.weighted_loss(inp["token_loss"], lab)
+    valid = lab != -100
+    assert good[0] == 0 and np.isnan(rl[0]) and np.isfinite(loss)
+    assert abs(loss - inp["token_loss"][valid].astype(np.float64).sum() / valid.sum()) < 1e-12 * loss
+    loss0, rl0, good0, dtl0 = ref.weighted_loss(inp["token_loss"], np.full_like(lab, -100))
+    assert loss0 == 0.0 and not good0.any() and not dtl0.any() and np.isnan(rl0).all()
+
+
+# ---------------------------------------------------------------------------
+# Generator
+# ---------------------------------------------------------------------------
+
+def test_generator_lengths_and_positions():
+    assert configs.WORKLOADS[2].lengths() == [6945, 2521, 1351, 2804, 3690, 6766, 3978, 1218, 3084, 411]
+    assert configs.WORKLOADS[5].lengths() == [186631, 217417, 37964, 82276]
+    assert configs.WORKLOADS[2].allowed_pairs() == 75345846
+    assert configs.WORKLOADS[5].allowed_pairs() == 45156205905
+    pos = configs.WORKLOADS[2].position_ids()
+    assert pos.size == 32768 and (pos == 0).sum() == 10 and pos[6945] == 0 and pos[6944] == 6944
+
+
+def test_generator_bf16_rounding_matches_torch():
+    import torch
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32)
+    x[:4] = [1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 0.0]   # ties go to even
+    ours = gen.f32_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+    assert list(ours[:3]) == [0x3F80, 0x3F82, 0xBF80]
+
+
+def test_generator_is_deterministic_and_chunked():
+    a = gen.normal_bf16((1, 1), (gen.CHUNK + 5,))
+    b = gen.normal_bf16((1, 1), (gen.CHUNK + 5,))
+    assert np.array_equal(a, b)
+    tail = gen.f32_to_bf16_bits(np.random.default_rng([1, 1, 1]).standard_normal(5, dtype=np.float32))
+    assert np.array_equal(a[gen.CHUNK:], tail)
