@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's share of a Ulysses attention layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+seq->head relayout of Q and K/V for rank 0, segment bounds from position_ids,
+causal attention forward, head->seq of O, seq->head of dO, attention backward,
+head->seq of dQ and dK/dV, and the token-weighted loss over all ranks.
+Default workload: the 500K-token rank share at sp_size 8 (N=524288, 4 query
+heads, 1 KV head, d=128, 4 packed samples).
+
+Prints ONE JSON line.  `value` is attention fwd+bwd TFLOP/s over the whole
+step (algorithmic FLOPs 14*d*A*hq, A = allowed causal pairs per head).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBPS = 8000.0
+METRIC = "causal attn fwd+bwd TFLOP/s per rank-share (%MFMA peak); relayout GB/s (%HBM)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 5])
+    ap.add_argument("--relayout-reps", type=int, default=10,
+                    help="timed round trips of the relayout-bound workload (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=6144,
+                    help="tokens of the oracle's CPU-baseline sample (0: skip)")
+    return ap.parse_args()
+
+
+def to_dev_bf16(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def cpu_baseline(w, tokens):
+    """The oracle's fwd+bwd on the first `tokens` tokens of the workload's first packed
+    sample (one causal sample, the workload's heads and head_dim), timed on the host."""
+    from oracle import ref
+    from synth import gen
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    L = min(tokens, w.lengths()[0])
+    q = gen.normal_bf16((w.cfg, 1), (L, w.hq, w.head_dim))
+    k = gen.normal_bf16((w.cfg, 2), (L, w.hkv, w.head_dim))
+    v = gen.normal_bf16((w.cfg, 3), (L, w.hkv, w.head_dim))
+    do = gen.normal_bf16((w.cfg, 4), (L, w.hq, w.head_dim))
+    pos = np.arange(L, dtype=np.int64)
+    t0 = time.perf_counter()
+    ref.attn_fwd(q, k, v, pos)
+    ref.attn_bwd(q, k, v, do, pos)
+    dt = time.perf_counter() - t0
+    A = L * (L + 1) // 2
+    flops = 14.0 * w.head_dim * A * w.hq
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"fp64 oracle attn_fwd+attn_bwd on one causal sample of {L} tokens "
+                      f"(the first {L} tokens of the workload's first packed sample), "
+                      f"hq={w.hq}, hkv={w.hkv}, d={w.head_dim}; {flops:.3e} algorithmic FLOP"}
+
+
+def relayout_bound(dev, reps):
+    """The relayout-bound workload: P=8, N=262144, 32 heads, d=128, fused QKV (G=3),
+    seq->head of all ranks then head->seq back, checked bit-exact on the device."""
+    import torch
+    from synth import configs
+    from ulysses_sequence_parallelism_share_amd import ops
+    w = configs.WORKLOADS[4]
+    x = to_dev_bf16(configs.relayout_inputs(w), dev)
+    h = torch.empty((w.sp_size, w.relayout_groups, w.n_tokens, w.relayout_heads // w.sp_size,
+                     w.head_dim), dtype=torch.bfloat16, device=dev)
+    back = torch.empty_like(x)
+    for _ in range(2):
+        ops.ulysses_seq_to_head(x, out=h)
+        ops.ulysses_head_to_seq(h, w.sp_size, out=back)
+    torch.cuda.synchronize()
+    ops.sp_timing_enable(True)
+    for _ in range(reps):
+        ops.ulysses_seq_to_head(x, out=h)
+        ops.ulysses_head_to_seq(h, w.sp_size, out=back)
+    torch.cuda.synchronize()
+    kt = ops.sp_timing_collect()
+    ops.sp_timing_enable(False)
+    exact = bool(torch.equal(back.view(torch.int16), x.view(torch.int16)))
+    nbytes = 2 * x.numel() * 2                      # read once + write once
+    out = {"workload": w.name, "bytes_per_direction": nbytes, "bit_exact_roundtrip": exact}
+    for key, name in (("seq_to_head", "relayout_seq_to_head"), ("head_to_seq", "relayout_head_to_seq")):
+        ms = kt[name]["avg_ms"]
+        out[key] = {"avg_ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm": nbytes / ms / 1e6 / PEAK_HBM_GBPS}
+    del x, h, back
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the all-to-all is emulated on one device); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import configs
+    from ulysses_sequence_parallelism_share_amd import ops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = configs.WORKLOADS[args.workload]
+    P, N, hq, hkv, d = w.sp_size, w.n_tokens, w.hq, w.hkv, w.head_dim
+    lengths = w.lengths()
+    A = w.allowed_pairs()
+    fwd_flop = 4.0 * d * A * hq
+    bwd_flop = 10.0 * d * A * hq
+    log(f"[bench] workload {w.name}: lengths {lengths}, A={A}")
+
+    t0 = time.time()
+    relayout_in_step = args.workload == 5
+    if relayout_in_step:
+        inp = configs.exchange_inputs(w)
+        q_seq = to_dev_bf16(inp.pop("q_seq"), dev)
+        kv_seq = to_dev_bf16(inp.pop("kv_seq"), dev)
+        do_seq = to_dev_bf16(inp.pop("do_seq"), dev)
+        qh = torch.empty((1, N, hq, d), dtype=torch.bfloat16, device=dev)
+        kvh = torch.empty((2, N, hkv, d), dtype=torch.bfloat16, device=dev)
+        doh = torch.empty((1, N, hq, d), dtype=torch.bfloat16, device=dev)
+        o_seq = torch.zeros_like(q_seq)
+        dq_seq = torch.zeros_like(q_seq)
+        dkv_seq = torch.zeros_like(kv_seq)
+    else:
+        inp = configs.rank_share_inputs(w)
+        qh = to_dev_bf16(inp.pop("q"), dev)[None]
+        kvh = torch.stack([to_dev_bf16(inp.pop("k"), dev), to_dev_bf16(inp.pop("v"), dev)])
+        doh = to_dev_bf16(inp.pop("do"), dev)[None]
+        q_seq = kv_seq = do_seq = o_seq = dq_seq = dkv_seq = None
+    pos = torch.from_numpy(inp["pos"]).to(dev)
+    lw = configs.Workload(w.cfg, w.name, P, N, hq, hkv, d, prompt_frac=0.1)
+    li = configs.loss_inputs(lw)
+    token_loss = torch.from_numpy(li["token_loss"]).to(dev)
+    labels = torch.from_numpy(li["shift_labels"]).to(dev)
+    o = torch.empty((N, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((hq, N), dtype=torch.float32, device=dev)
+    dq = torch.empty((1, N, hq, d), dtype=torch.bfloat16, device=dev)
+    dkv = torch.empty((2, N, hkv, d), dtype=torch.bfloat16, device=dev)
+    ws = ops.workspace(N, hq, hkv, d, dev)
+    loss_out = (torch.empty(1, dtype=torch.float32, device=dev),
+                torch.empty(P, dtype=torch.float32, device=dev),
+                torch.empty(P, dtype=torch.int64, device=dev),
+                torch.empty((P, N // P), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
+
+    relayout_bytes = 0
+
+    def step():
+        nonlocal relayout_bytes
+        nb = 0
+        if relayout_in_step:
+            ops.ulysses_seq_to_head(q_seq, rank=0, out=qh)
+            ops.ulysses_seq_to_head(kv_seq, rank=0, out=kvh)
+            nb += 2 * 2 * (qh.numel() + kvh.numel())
+        ops.sp_attn_fwd(qh[0], kvh[0], kvh[1], pos, o=o, lse=lse, ws=ws)
+        if relayout_in_step:
+            ops.ulysses_head_to_seq(o[None], P, rank=0, out=o_seq)
+            ops.ulysses_seq_to_head(do_seq, rank=0, out=doh)
+            nb += 2 * 2 * (o.numel() + doh.numel())
+        ops.sp_attn_bwd(qh[0], kvh[0], kvh[1], o, doh[0], lse, pos, grad_dtype=torch.bfloat16,
+                        dq=dq[0], dk=dkv[0], dv=dkv[1], ws=ws)
+        if relayout_in_step:
+            ops.ulysses_head_to_seq(dq, P, rank=0, out=dq_seq)
+            ops.ulysses_head_to_seq(dkv, P, rank=0, out=dkv_seq)
+            nb += 2 * 2 * (dq.numel() + dkv.numel())
+        ops.sp_weighted_loss(token_loss, labels, out=loss_out)
+        relayout_bytes = nb
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+    ops.sp_timing_enable(True)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kt = ops.sp_timing_collect()
+    ops.sp_timing_enable(False)
+    log(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step")
+
+    per_step = {k: v["total_ms"] / args.steps for k, v in kt.items()}
+    fwd_ms = kt["attn_fwd"]["avg_ms"]
+    dkdv_ms = kt["attn_bwd_dkdv"]["avg_ms"]
+    dq_ms = kt["attn_bwd_dq"]["avg_ms"]
+    attn_kernel_ms = sum(per_step.get(n, 0.0) for n in
+                         ("segments", "transpose_rows", "attn_fwd", "bwd_delta", "attn_bwd_dkdv",
+                          "attn_bwd_dq"))
+    algo = {"attn_fwd": fwd_flop, "attn_bwd_dkdv": 0.8 * bwd_flop, "attn_bwd_dq": 0.2 * bwd_flop}
+    dom = max(algo, key=lambda n: kt[n]["avg_ms"])
+    dom_tflops = algo[dom] / kt[dom]["avg_ms"] / 1e9
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_ms": kt[dom]["avg_ms"], "algorithmic_flop_per_launch": algo[dom]}
+    value = (fwd_flop + bwd_flop) / ms_per_step / 1e9
+    attention = {
+        "fwd_flop": fwd_flop, "bwd_flop": bwd_flop,
+        "attn_fwd_ms": fwd_ms, "attn_bwd_dkdv_ms": dkdv_ms, "attn_bwd_dq_ms": dq_ms,
+        "fwd_kernel_tflops": fwd_flop / fwd_ms / 1e9,
+        "bwd_kernels_tflops": bwd_flop / (dkdv_ms + dq_ms) / 1e9,
+        "attention_calls_ms": attn_kernel_ms,
+        "tflops_attention_kernels": (fwd_flop + bwd_flop) / attn_kernel_ms / 1e9,
+        "frac_mfma_attention_kernels": (fwd_flop + bwd_flop) / attn_kernel_ms / 1e9 / PEAK_BF16_TFLOPS,
+        "frac_mfma_step": value / PEAK_BF16_TFLOPS,
+    }
+    relayout = None
+    if relayout_in_step:
+        rl_ms = per_step.get("relayout_seq_to_head", 0.0) + per_step.get("relayout_head_to_seq", 0.0)
+        relayout = {"step_bytes": relayout_bytes, "step_ms": rl_ms,
+                    "step_GB/s": relayout_bytes / rl_ms / 1e6,
+                    "step_frac_hbm": relayout_bytes / rl_ms / 1e6 / PEAK_HBM_GBPS}
+    del q_seq, kv_seq, do_seq, o_seq, dq_seq, dkv_seq
+    torch.cuda.empty_cache()
+
+    relayout_bound_out = None
+    if args.relayout_reps > 0:
+        t1 = time.time()
+        relayout_bound_out = relayout_bound(dev, args.relayout_reps)
+        log(f"[bench] relayout-bound workload done in {time.time() - t1:.1f}s")
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        t1 = time.time()
+        cpu = cpu_baseline(w, args.cpu_tokens)
+        log(f"[bench] cpu baseline done in {time.time() - t1:.1f}s")
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_tokens": N, "sp_size": P, "hq": hq, "hkv": hkv,
+                   "head_dim": d, "sample_lengths": lengths, "allowed_pairs_per_head": A,
+                   "grad_dtype": "bf16", "parallelism": "one rank's share (Ulysses sp_size "
+                   f"{P}) on 1 GPU; all-to-all emulated on device"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "attention": attention,
+        "relayout_step": relayout,
+        "relayout_bound": relayout_bound_out,
+        "kernels_ms_per_step": per_step,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+// C ABI of the library: argument checks, workspace layout and launches.
+// Every check runs on the host before anything is enqueued, so an invalid
+// call returns an error without touching the device (and works on a host
+// without a GPU).  The rules follow the pages' problem statement: the
+// sequence is padded to a multiple of sp_size and the head count must be
+// divisible by sp_size (Transformers guide "Ulysses sequence parallelism",
+// "Configuration"); masking comes from position_ids only.
+#include <math.h>
+
+#include "../../include/ulysses_sp.h"
+#include "launch.h"
+
+namespace {
+
+inline bool misaligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; }
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;  // token and virtual-row indices stay in int32
+
+sp_status check_relayout(const void *src, const void *dst, int P, int64_t N, int G, int H, int d,
+                         int rank) {
+    if (P < 1 || N < 0 || G < 1 || H < 1 || d < 1) return SP_E_SHAPE;
+    if (N % P != 0 || H % P != 0) return SP_E_NOT_DIVISIBLE;
+    if (rank < -1 || rank >= P) return SP_E_RANK;
+    const int64_t piece = (int64_t)(H / P) * d;
+    if (piece % 8 != 0) return SP_E_SHAPE;
+    if (N >= kMaxRows || (int64_t)G * H * d / 8 >= ((int64_t)1 << 24)) return SP_E_SHAPE;
+    if (N == 0) return SP_OK;
+    if (src == nullptr || dst == nullptr) return SP_E_NULL;
+    if (misaligned(src, 16) || misaligned(dst, 16)) return SP_E_ALIGN;
+    return SP_OK;
+}
+
+sp_status check_attn_shape(int64_t N, int hq, int hkv, int d, float scale) {
+    if (N < 0 || hq < 1 || hkv < 1) return SP_E_SHAPE;
+    if (d != 64 && d != 128) return SP_E_SHAPE;
+    if (hq % hkv != 0) return SP_E_NOT_DIVISIBLE;
+    if (N * (int64_t)hq >= kMaxRows) return SP_E_SHAPE;
+    if (!(scale >= 0.f) || isinf(scale)) return SP_E_SHAPE;
+    return SP_OK;
+}
+
+inline int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws) {
+    const int g = hq / hkv;
+    const int64_t Npad = pad64(N), Mpad = pad64(N * g);
+    size_t off = 0;
+    char *b = (char *)base;
+    auto take = [&](size_t bytes) {
+        char *p = b ? b + off : nullptr;
+        off += align256(bytes);
+        return (void *)p;
+    };
+    AttnWorkspace w;
+    w.kstart = (int32_t *)take(4 * (size_t)N);
+    w.kend = (int32_t *)take(4 * (size_t)N);
+    w.kvt = take(2 * (size_t)hkv * d * Npad);
+    w.qt = take(2 * (size_t)hkv * d * Mpad);
+    w.dot = take(2 * (size_t)hkv * d * Mpad);
+    w.delta = (float *)take(4 * (size_t)hq * N);
+    if (ws) *ws = w;
+    return off;
+}
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+const char *sp_status_string(int status) {
+    switch (status) {
+        case SP_OK: return "ok";
+        case SP_E_NULL: return "a required pointer is NULL";
+        case SP_E_SHAPE: return "a size is negative or unsupported";
+        case SP_E_NOT_DIVISIBLE: return "n_tokens or n_heads not divisible by sp_size, or query heads not divisible by KV heads";
+        case SP_E_ALIGN: return "a pointer is not suitably aligned";
+        case SP_E_RANK: return "rank outside [-1, sp_size)";
+        case SP_E_WORKSPACE: return "workspace missing or too small";
+        case SP_E_HIP: return "a HIP launch failed";
+        case SP_E_DTYPE: return "unknown element type";
+        default: return "unknown status";
+    }
+}
+
+int sp_abi_version(void) { return 1; }
+
+sp_status ulysses_seq_to_head(const void *x_seq, void *x_head, int sp_size, int64_t n_tokens,
+                              int n_groups, int n_heads, int head_dim, int rank,
+                              hipStream_t stream) {
+    sp_status st = check_relayout(x_seq, x_head, sp_size, n_tokens, n_groups, n_heads, head_dim, rank);
+    if (st != SP_OK || n_tokens == 0) return st;
+    return launch_relayout(true, x_seq, x_head, sp_size, n_tokens, n_groups, n_heads, head_dim,
+                           rank, stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
+sp_status ulysses_head_to_seq(const void *x_head, void *x_seq, int sp_size, int64_t n_tokens,
+                              int n_groups, int n_heads, int head_dim, int rank,
+                              hipStream_t stream) {
+    sp_status st = check_relayout(x_head, x_seq, sp_size, n_tokens, n_groups, n_heads, head_dim, rank);
+    if (st != SP_OK || n_tokens == 0) return st;
+    return launch_relayout(false, x_head, x_seq, sp_size, n_tokens, n_groups, n_heads, head_dim,
+                           rank, stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
+size_t sp_attn_workspace_bytes(int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim) {
+    if (check_attn_shape(n_tokens, n_q_heads, n_kv_heads, head_dim, 0.f) != SP_OK) return 0;
+    return attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, nullptr, nullptr);
+}
+
+sp_status sp_attn_fwd(const void *q, const void *k, const void *v, const int64_t *position_ids,
+                      int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                      float softmax_scale, void *o, float *lse, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    sp_status st = check_attn_shape(n_tokens, n_q_heads, n_kv_heads, head_dim, softmax_scale);
+    if (st != SP_OK || n_tokens == 0) return st;
+    if (!q || !k || !v || !position_ids || !o || !lse) return SP_E_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(position_ids, 8) || misaligned(lse, 4))
+        return SP_E_ALIGN;
+    const size_t need = attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, nullptr, nullptr);
+    if (!workspace || workspace_bytes < need) return SP_E_WORKSPACE;
+    if (misaligned(workspace, 16)) return SP_E_ALIGN;
+    AttnWorkspace ws;
+    attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, workspace, &ws);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+    return launch_attn_fwd(q, k, v, position_ids, n_tokens, n_q_heads, n_kv_heads, head_dim,
+                           scale, o, lse, ws, stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
+sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *d_o,
+                      const float *lse, const int64_t *position_ids, int64_t n_tokens,
+                      int n_q_heads, int n_kv_heads, int head_dim, float softmax_scale,
+                      int grad_dtype, void *dq, void *dk, void *dv, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    sp_status st = check_attn_shape(n_tokens, n_q_heads, n_kv_heads, head_dim, softmax_scale);
+    if (st != SP_OK) return st;
+    if (grad_dtype != SP_DTYPE_BF16 && grad_dtype != SP_DTYPE_F32) return SP_E_DTYPE;
+    if (n_tokens == 0) return SP_OK;
+    if (!q || !k || !v || !o || !d_o || !lse || !position_ids || !dq || !dk || !dv) return SP_E_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(d_o, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
+        misaligned(position_ids, 8) || misaligned(lse, 4))
+        return SP_E_ALIGN;
+    const size_t need = attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, nullptr, nullptr);
+    if (!workspace || workspace_bytes < need) return SP_E_WORKSPACE;
+    if (misaligned(workspace, 16)) return SP_E_ALIGN;
+    AttnWorkspace ws;
+    attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, workspace, &ws);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+    return launch_attn_bwd(q, k, v, o, d_o, lse, position_ids, n_tokens, n_q_heads, n_kv_heads,
+                           head_dim, scale, grad_dtype == SP_DTYPE_F32, dq, dk, dv, ws,
+                           stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
+sp_status sp_weighted_loss(const float *token_loss, const int64_t *shift_labels, int sp_size,
+                           int64_t n_tokens, int64_t ignore_index, float *loss, float *rank_loss,
+                           int64_t *good_tokens, float *d_token_loss, hipStream_t stream) {
+    if (sp_size < 1 || n_tokens < 0) return SP_E_SHAPE;
+    if (n_tokens % sp_size != 0) return SP_E_NOT_DIVISIBLE;
+    if (!loss || !rank_loss || !good_tokens) return SP_E_NULL;
+    if (n_tokens > 0 && (!token_loss || !shift_labels)) return SP_E_NULL;
+    if (misaligned(token_loss, 4) || misaligned(shift_labels, 8) || misaligned(loss, 4) ||
+        misaligned(rank_loss, 4) || misaligned(good_tokens, 8) || misaligned(d_token_loss, 4))
+        return SP_E_ALIGN;
+    return launch_weighted_loss(token_loss, shift_labels, sp_size, n_tokens, ignore_index, loss,
+                                rank_loss, good_tokens, d_token_loss, stream) == hipSuccess
+               ? SP_OK : SP_E_HIP;
+}
+
+}  // extern "C"
+#pragma GCC visibility pop

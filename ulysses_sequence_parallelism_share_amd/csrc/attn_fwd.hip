@@ -1,0 +1,218 @@
+// Causal attention forward for one rank's heads over the full sequence
+// (blog "Ulysses Sequence Parallelism: Training with Million-Token
+// Contexts", "How Ulysses works", step 4: each GPU runs standard attention
+// for its heads over all positions).  Masking comes from position_ids
+// through the segment bounds (Transformers guide "Ulysses sequence
+// parallelism", "Configuration": position_ids replace the 4D mask and
+// packed samples must not attend across their boundaries).
+//
+// Design (gfx950, 64-wide waves, MFMA 32x32x16 bf16):
+//  * GQA rows are folded together: for KV head kh the g = hq/hkv query heads
+//    that share it form "virtual rows" v = t*g + (h - kh*g).  A workgroup
+//    owns 128 consecutive virtual rows (4 waves x 32), so every K/V tile it
+//    stages in LDS serves all g heads, and the causal bound of the tile
+//    spans only 128/g tokens.
+//  * Each wave computes S^T = K Q^T (keys x queries), so a lane owns one
+//    query column: the row max and row sum of the softmax are per-lane
+//    register reductions plus one exchange with lane l^32.
+//  * The probabilities leave the S^T accumulators directly as the B operand
+//    of O^T += V^T P^T; V^T is pre-transposed with the matching key order
+//    (perm16), and the per-row rescale of O is a per-lane multiply.
+//  * fp32 online softmax in the log2 domain (scale * log2(e) folded into one
+//    multiply, exponentials with v_exp_f32).
+//  * Tiles inside every row's segment and below every row's diagonal skip
+//    the mask; the key range of a workgroup is [kstart(first row), last row].
+//  * Workgroups are launched longest-first (last row tiles first).
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int BM = 128;  // virtual query rows per workgroup (4 waves x 32)
+constexpr int BN = 64;   // keys per tile
+constexpr int kThreads = 256;
+
+template <int D>
+struct FwdTiles {
+    bf16 k[BN][D + 8];    // keys x features; +16 B per row keeps the A reads conflict-free
+    bf16 vt[D][BN + 8];   // features x keys (perm16 key order)
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_attn_fwd(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ vt,
+    const int32_t *__restrict__ kstart, bf16 *__restrict__ o, float *__restrict__ lse, int N,
+    int Npad, int hq, int hkv, int g, FastDiv fg, float scale_log2, int n_row_tiles) {
+    __shared__ FwdTiles<D> sm;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 31, half = lane >> 5;
+    const int kh = blockIdx.x % hkv;
+    const int tile = n_row_tiles - 1 - blockIdx.x / hkv;
+    const int M = N * g;
+    const int v0 = tile * BM;
+    const int vrow = v0 + wave * 32 + col;
+    const bool row_ok = vrow < M;
+    const int vr = row_ok ? vrow : M - 1;
+    const int t = (int)fdiv((uint32_t)vr, fg);
+    const int h = kh * g + (vr - t * g);
+    const int t_first = (int)fdiv((uint32_t)v0, fg);
+    const int t_last = (int)fdiv((uint32_t)(min(v0 + BM, M) - 1), fg);
+    const int key_lo = kstart[t_first];
+    const int ks_max = kstart[t_last];
+    const int my_ks = kstart[t];
+
+    // This lane's query row as the B operand of S^T = K Q^T.
+    bf16x8 qf[D / 16];
+    {
+        const bf16 *qrow = q + ((size_t)t * hq + h) * D + half * 8;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) qf[s] = *(const bf16x8 *)(qrow + 16 * s);
+    }
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+    float m_run = -1e30f, l_run = 0.f;
+
+    // Register staging of the next tile while the current one is computed.
+    constexpr int KV = BN * D / 8 / kThreads;
+    u32x4 kreg[KV], vreg[KV];
+    auto load_tile = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+            const int x = tid + i * kThreads;
+            const int r = x / (D / 8), c = x % (D / 8);
+            const int j = j0 + r;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            kreg[i] = j < N ? *(const u32x4 *)(k + ((size_t)j * hkv + kh) * D + c * 8) : z;
+        }
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+            const int x = tid + i * kThreads;
+            const int r = x / (BN / 8), c = x % (BN / 8);
+            vreg[i] = *(const u32x4 *)(vt + ((size_t)kh * D + r) * Npad + j0 + c * 8);
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+            const int x = tid + i * kThreads;
+            *(u32x4 *)&sm.k[x / (D / 8)][(x % (D / 8)) * 8] = kreg[i];
+            *(u32x4 *)&sm.vt[x / (BN / 8)][(x % (BN / 8)) * 8] = vreg[i];
+        }
+    };
+
+    const int jt0 = key_lo / BN, jt1 = t_last / BN;
+    load_tile(jt0 * BN);
+    for (int jt = jt0; jt <= jt1; ++jt) {
+        const int j0 = jt * BN;
+        __syncthreads();
+        store_tile();
+        __syncthreads();
+        if (jt < jt1) load_tile(j0 + BN);
+        const bool full = (j0 + BN - 1 <= t_first) && (j0 >= ks_max);
+
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                const bf16x8 a = *(const bf16x8 *)&sm.k[kb * 32 + col][16 * st + 8 * half];
+                s[kb] = mfma32(a, qf[st], s[kb]);
+            }
+        }
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = s[kb][r] * scale_log2;
+                if (!full) {
+                    const int key = j0 + kb * 32 + acc_row(r, half);
+                    if (key < my_ks || key > t) x = -INFINITY;
+                }
+                s[kb][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = wave_max_pair(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(s[kb][r] - m_new);
+                l_run += p;
+                pf[kb][r >> 3][r & 7] = (bf16)p;
+            }
+
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const bf16x8 a =
+                        *(const bf16x8 *)&sm.vt[db * 32 + col][kb * 32 + s2 * 16 + half * 8];
+                    oacc[db] = mfma32(a, pf[kb][s2], oacc[db]);
+                }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.f / l_tot;
+    if (row_ok) {
+        bf16 *orow = o + ((size_t)t * hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                bf16x4 w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = (bf16)(oacc[db][rg * 4 + i] * inv);
+                *(bf16x4 *)(orow + db * 32 + rg * 8 + half * 4) = w;
+            }
+        if (half == 0) lse[(size_t)h * N + t] = (m_run + log2f(l_tot)) * SP_LN2;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const int64_t *pos,
+                           int64_t N, int hq, int hkv, int d, float scale, void *o, float *lse,
+                           const AttnWorkspace &ws, hipStream_t stream) {
+    if (N <= 0) return hipSuccess;
+    hipError_t e = launch_segments(pos, ws.kstart, ws.kend, N, stream);
+    if (e != hipSuccess) return e;
+    const int64_t Npad = (N + 63) / 64 * 64;
+    e = launch_transpose_rows(v, ws.kvt, N, hkv, hkv, 1, d, Npad, stream);
+    if (e != hipSuccess) return e;
+    const int g = hq / hkv;
+    const int M = (int)(N * g);
+    const int n_row_tiles = (M + BM - 1) / BM;
+    const FastDiv fg = make_fastdiv((uint32_t)g);
+    const float scale_log2 = scale * SP_LOG2E;
+    const dim3 grid((unsigned)(n_row_tiles * hkv));
+    KernelTimer timer("attn_fwd", stream);
+    if (d == 128)
+        hipLaunchKernelGGL(k_attn_fwd<128>, grid, dim3(kThreads), 0, stream, (const bf16 *)q,
+                           (const bf16 *)k, (const bf16 *)ws.kvt, ws.kstart, (bf16 *)o, lse,
+                           (int)N, (int)Npad, hq, hkv, g, fg, scale_log2, n_row_tiles);
+    else
+        hipLaunchKernelGGL(k_attn_fwd<64>, grid, dim3(kThreads), 0, stream, (const bf16 *)q,
+                           (const bf16 *)k, (const bf16 *)ws.kvt, ws.kstart, (bf16 *)o, lse,
+                           (int)N, (int)Npad, hq, hkv, g, fg, scale_log2, n_row_tiles);
+    return hipGetLastError();
+}

@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).  All
+// arguments have been validated by the C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// RAII: brackets one kernel launch with HIP events on its stream when the
+// library's timing mode is on (sp_timing_enable); otherwise does nothing.
+class KernelTimer {
+  public:
+    KernelTimer(const char *name, hipStream_t s);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer &) = delete;
+    KernelTimer &operator=(const KernelTimer &) = delete;
+
+  private:
+    const char *name_;
+    hipStream_t s_;
+    hipEvent_t a_, b_;
+};
+
+hipError_t launch_relayout(bool to_head, const void *src, void *dst, int P, int64_t N, int G,
+                           int H, int d, int rank, hipStream_t stream);
+
+hipError_t launch_transpose_rows(const void *src, void *dst, int64_t N, int heads_src, int n_kv,
+                                 int g, int D, int64_t rows_pad, hipStream_t stream);
+
+hipError_t launch_segments(const int64_t *pos, int32_t *kstart, int32_t *kend, int64_t N,
+                           hipStream_t stream);
+
+// Workspace layout shared by the forward and backward calls.
+struct AttnWorkspace {
+    int32_t *kstart;   // [N]
+    int32_t *kend;     // [N]
+    void *kvt;         // fwd: V^T; bwd: K^T        [hkv][d][Npad]   bf16, keys permuted
+    void *qt;          // bwd: Q^T                  [hkv][d][Mpad]   bf16, virtual rows permuted
+    void *dot;         // bwd: dO^T                 [hkv][d][Mpad]
+    float *delta;      // bwd: D = rowsum(dO * O)   [hq][N]          fp32
+};
+
+size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws);
+
+hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const int64_t *pos,
+                           int64_t N, int hq, int hkv, int d, float scale, void *o, float *lse,
+                           const AttnWorkspace &ws, hipStream_t stream);
+
+hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                           const void *d_o, const float *lse, const int64_t *pos, int64_t N,
+                           int hq, int hkv, int d, float scale, bool grad_f32, void *dq,
+                           void *dk, void *dv, const AttnWorkspace &ws, hipStream_t stream);
+
+hipError_t launch_weighted_loss(const float *token_loss, const int64_t *labels, int P, int64_t N,
+                                int64_t ignore_index, float *loss, float *rank_loss,
+                                int64_t *good, float *d_token_loss, hipStream_t stream);
