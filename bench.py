@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=5, choices=[2, 3, 5])
     ap.add_argument("--relayout-reps", type=int, default=10,
                     help="timed round trips of the relayout-bound workload (0: skip)")
-    ap.add_argument("--cpu-tokens", type=int, default=6144,
+    ap.add_argument("--cpu-tokens", type=int, default=20480,
                     help="tokens of the oracle's CPU-baseline sample (0: skip)")
     return ap.parse_args()
 

@@ -200,9 +200,10 @@ sp_status sp_weighted_loss(const float *token_loss, const int64_t *shift_labels,
  * setting.  This is the only process-wide state of the library.
  *
  * sp_timing_collect waits for the recorded events, aggregates them per
- * kernel name into `out` (up to max_entries entries; `out` may be NULL to
- * count), clears the records and returns the number of distinct kernels, or
- * -1 if an event could not be read.  Host memory.
+ * kernel name into `out` (up to max_entries entries), clears the records and
+ * returns the number of distinct kernels, or -1 if an event could not be
+ * read.  With out == NULL it only returns the count and keeps the records.
+ * `out` is host memory.
  */
 typedef struct sp_kernel_time {
     char name[48];

@@ -101,13 +101,15 @@ int sp_timing_collect(sp_kernel_time *out, int max_entries) {
         slot->total_ms += ms;
         if (ms < slot->min_ms) slot->min_ms = ms;
         if (ms > slot->max_ms) slot->max_ms = ms;
+    }
+    const int n = (int)agg.size();
+    if (out == nullptr) return n;            // a count query keeps the records
+    for (int i = 0; i < n && i < max_entries; ++i) out[i] = agg[i];
+    for (auto &r : g_recs) {
         g_pool.push_back(r.a);
         g_pool.push_back(r.b);
     }
     g_recs.clear();
-    const int n = (int)agg.size();
-    if (out)
-        for (int i = 0; i < n && i < max_entries; ++i) out[i] = agg[i];
     return n;
 }
 
