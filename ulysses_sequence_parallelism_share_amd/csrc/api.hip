@@ -60,7 +60,9 @@ size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, Attn
     w.kvt = take(2 * (size_t)hkv * d * Npad);
     w.qt = take(2 * (size_t)hkv * d * Mpad);
     w.dot = take(2 * (size_t)hkv * d * Mpad);
-    w.delta = (float *)take(4 * (size_t)hq * N);
+    w.qv = hkv > 1 ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
+    w.dov = hkv > 1 ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
+    w.rowstat = (float2 *)take(8 * (size_t)hkv * Mpad);
     if (ws) *ws = w;
     return off;
 }

@@ -19,66 +19,85 @@
 //  * k_attn_bwd_dq - a workgroup owns 128 virtual query rows (like the
 //    forward); Q and dO stay in registers, K, V and K^T tiles stream through
 //    LDS, and dQ^T += K^T dS^T accumulates per lane.
+// Both stream their tiles through double-buffered LDS filled by direct
+// global->LDS loads one tile ahead.  A pre-pass writes, per virtual row,
+// (lse * log2e, D) contiguously, so a row tile's statistics are one load.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
+#include "tile.h"
 
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int BK = 128;  // keys per dK/dV workgroup
 constexpr int BQ = 32;   // virtual query rows per dK/dV tile
 constexpr int BM = 128;  // virtual query rows per dQ workgroup
 constexpr int BN = 64;   // keys per dQ tile
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O): one group of D/8 lanes per (token, head) row.
+// Row statistics: rowstat[kh][v] = (lse * log2e, rowsum(dO * O)) for every
+// virtual row v < Mpad of KV head kh; rows past M get (+inf, 0), so their
+// probabilities are exactly 0.  One group of D/8 lanes per row.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_bwd_delta(const bf16 *__restrict__ o,
-                                                        const bf16 *__restrict__ d_o,
-                                                        float *__restrict__ delta, int N,
-                                                        int hq) {
+__global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restrict__ o,
+                                                           const bf16 *__restrict__ d_o,
+                                                           const float *__restrict__ lse,
+                                                           float2 *__restrict__ rowstat, int N,
+                                                           int hq, int hkv, int g, FastDiv fg,
+                                                           int Mpad) {
     constexpr int LPR = D / 8;
-    const int64_t row = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / LPR;
+    const int64_t row = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / LPR;  // kh*Mpad + v
     const int c = threadIdx.x % LPR;
-    const bool ok = row < (int64_t)N * hq;
+    const bool in_grid = row < (int64_t)hkv * Mpad;
+    const int kh = in_grid ? (int)(row / Mpad) : 0;
+    const int v = in_grid ? (int)(row - (int64_t)kh * Mpad) : 0;
+    const bool ok = in_grid && v < N * g;
     float acc = 0.f;
+    int t = 0, h = 0;
     if (ok) {
-        const bf16x8 a = *(const bf16x8 *)(o + row * D + c * 8);
-        const bf16x8 b = *(const bf16x8 *)(d_o + row * D + c * 8);
+        t = (int)fdiv((uint32_t)v, fg);
+        h = kh * g + (v - t * g);
+        const size_t off = ((size_t)t * hq + h) * D + c * 8;
+        const bf16x8 a = *(const bf16x8 *)(o + off);
+        const bf16x8 b = *(const bf16x8 *)(d_o + off);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc += (float)a[i] * (float)b[i];
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (ok && c == 0) {
-        const int t = (int)(row / hq), h = (int)(row % hq);
-        delta[(size_t)h * N + t] = acc;
-    }
+    if (in_grid && c == 0)
+        rowstat[row] = ok ? make_float2(lse[(size_t)h * N + t] * SP_LOG2E, acc)
+                          : make_float2(INFINITY, 0.f);
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
 template <int D>
-struct DkdvTiles {
-    bf16 q[BQ][D + 8];
-    bf16 dO[BQ][D + 8];
-    bf16 qt[D][BQ + 8];
-    bf16 dot[D][BQ + 8];
-    float lse2[BQ];
-    float delta[BQ];
+struct DkdvSmem {
+    using R = SwzTile<BQ, D / 8>;    // Q or dO rows of the tile
+    using T = SwzTile<D, BQ / 8>;    // Q^T or dO^T (features x rows, perm16 order)
+    static constexpr int kQ = 0, kDO = R::kBytes, kQT = 2 * R::kBytes,
+                         kDOT = 2 * R::kBytes + T::kBytes, kStat = 2 * R::kBytes + 2 * T::kBytes;
+    static constexpr int kStage = kStat + 1024;   // (lse2, D) of BQ rows: one wave-wide load
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ d_o, const bf16 *__restrict__ qt, const bf16 *__restrict__ dot,
-    const float *__restrict__ lse, const float *__restrict__ delta,
-    const int32_t *__restrict__ kend, void *__restrict__ dk, void *__restrict__ dv, int N,
-    int Mpad, int hq, int hkv, int g, FastDiv fg, float scale_log2, float scale, int out_f32) {
-    __shared__ DkdvTiles<D> sm;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bf16 *__restrict__ d_o, const bf16 *__restrict__ qv, const bf16 *__restrict__ dov,
+    size_t v_head_stride, int v_rows, const bf16 *__restrict__ qt, const bf16 *__restrict__ dot,
+    const float2 *__restrict__ rowstat, const int32_t *__restrict__ kend,
+    void *__restrict__ dk, void *__restrict__ dv, int N, int Mpad, int hq, int hkv, int g,
+    FastDiv fg, float scale_log2, float scale, int out_f32) {
+    using S = DkdvSmem<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int kh = blockIdx.x % hkv;
     const int j0 = (blockIdx.x / hkv) * BK;
@@ -90,8 +109,31 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
     const int kw1 = min(kw0 + 31, N - 1);               // and last (if kw0 < N)
     const bool wave_has_keys = kw0 < N;
     const int kend_w0 = wave_has_keys ? kend[kw0] : 0;
-    const int kend_w1 = wave_has_keys ? kend[kw1] : 0;
     const int kend_max = kend[min(j0 + BK, N) - 1];
+
+    // Rows [j0*g, kend_max*g) can see these keys; j0*g is a multiple of BQ.
+    const int vq_lo = j0 * g;
+    const int n_it = (kend_max * g - vq_lo + BQ - 1) / BQ;
+    // Q and dO rows come from virtual-row-major copies (row v of KV head kh at
+    // qv + kh*v_head_stride + v*D; `v_rows` rows exist).  Rows past the end
+    // are read from the last row: finite data, and their statistics make P
+    // exactly 0.
+    auto stage = [&](int it, int buf) {
+        char *base = smem + buf * S::kStage;
+        const int vq0 = vq_lo + it * BQ;
+        const size_t roff = (size_t)kh * v_head_stride + (size_t)vq0 * D;
+        stage_rows_async<BQ, D / 8, kWaves>(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
+        stage_rows_async<BQ, D / 8, kWaves>(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
+        stage_rows_async<D, BQ / 8, kWaves>(base + S::kQT, wave, lane,
+                                            qt + (size_t)kh * D * Mpad + vq0, (size_t)Mpad * 2, D);
+        stage_rows_async<D, BQ / 8, kWaves>(base + S::kDOT, wave, lane,
+                                            dot + (size_t)kh * D * Mpad + vq0, (size_t)Mpad * 2, D);
+        if (wave == kWaves - 1 && lane < BQ * 8 / 16)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)((const char *)(rowstat + (size_t)kh * Mpad + vq0) + lane * 16),
+                (lds_byte *)(base + S::kStat), 16, 0, 0);
+    };
+    if (n_it > 0) stage(0, 0);
 
     bf16x8 kf[D / 16], vf[D / 16];
     {
@@ -114,99 +156,73 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
 #pragma unroll
         for (int r = 0; r < 16; ++r) dkacc[i][r] = dvacc[i][r] = 0.f;
 
-    constexpr int RV = BQ * D / 8 / kThreads;  // 16-byte vectors per thread per row tile
-    const int vq_hi = kend_max * g;            // rows [j0*g, kend_max*g) can see these keys
-    for (int vq0 = j0 * g; vq0 < vq_hi; vq0 += BQ) {
+    for (int it = 0; it < n_it; ++it) {
+        wait_async();
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < RV; ++i) {
-            const int x = tid + i * kThreads;
-            const int r = x / (D / 8), c = x % (D / 8);
-            const int vv = vq0 + r;
-            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-            if (vv < M) {
-                const int t = (int)fdiv((uint32_t)vv, fg);
-                const size_t off = ((size_t)t * hq + kh * g + (vv - t * g)) * D + c * 8;
-                a = *(const u32x4 *)(q + off);
-                b = *(const u32x4 *)(d_o + off);
-            }
-            *(u32x4 *)&sm.q[r][c * 8] = a;
-            *(u32x4 *)&sm.dO[r][c * 8] = b;
-        }
-#pragma unroll
-        for (int i = 0; i < RV; ++i) {
-            const int x = tid + i * kThreads;
-            const int e = x / (BQ / 8), c = x % (BQ / 8);
-            const size_t off = ((size_t)kh * D + e) * Mpad + vq0 + c * 8;
-            *(u32x4 *)&sm.qt[e][c * 8] = *(const u32x4 *)(qt + off);
-            *(u32x4 *)&sm.dot[e][c * 8] = *(const u32x4 *)(dot + off);
-        }
-        if (tid < BQ) {
-            const int vv = vq0 + tid;
-            float l2 = INFINITY, dl = 0.f;
-            if (vv < M) {
-                const int t = (int)fdiv((uint32_t)vv, fg);
-                const size_t idx = (size_t)(kh * g + (vv - t * g)) * N + t;
-                l2 = lse[idx] * SP_LOG2E;
-                dl = delta[idx];
-            }
-            sm.lse2[tid] = l2;
-            sm.delta[tid] = dl;
-        }
-        __syncthreads();
-
+        if (it + 1 < n_it) stage(it + 1, (it + 1) & 1);
+        const char *base = smem + (it & 1) * S::kStage;
+        const int vq0 = vq_lo + it * BQ;
         const int tq_first = (int)fdiv((uint32_t)vq0, fg);
         const int tq_last = (int)fdiv((uint32_t)(min(vq0 + BQ, M) - 1), fg);
-        // every pair masked: all rows before the wave's keys, or past their samples
-        const bool skip = !wave_has_keys || tq_last < kw0 || tq_first >= kend_w1;
-        if (skip) continue;
-        const bool full = (kw1 <= tq_first) && (tq_last < kend_w0);
+        // A wave whose pairs are all masked still runs (its P is exactly 0):
+        // that keeps the loop free of divergent exits; it happens only on
+        // the diagonal and at sample ends.
+        const bool full = wave_has_keys && (kw1 <= tq_first) && (tq_last < kend_w0);
 
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            const bf16x8 a = *(const bf16x8 *)&sm.q[col][16 * st + 8 * half];
+            const int off = S::R::off(col, 2 * st + half);
+            const bf16x8 a = *(const bf16x8 *)(base + S::kQ + off);
+            const bf16x8 b = *(const bf16x8 *)(base + S::kDO + off);
             s = mfma32(a, kf[st], s);
-        }
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const bf16x8 a = *(const bf16x8 *)&sm.dO[col][16 * st + 8 * half];
-            dp = mfma32(a, vf[st], dp);
+            dp = mfma32(b, vf[st], dp);
         }
 
+        // rows of accumulator register r: rg*8 + half*4 + i (r = rg*4 + i)
         bf16x8 pf[2], dsf[2];
+        const f32x4 *stat = (const f32x4 *)(base + S::kStat);   // (lse2, D) of two rows
+        auto softmax = [&](auto masked) {
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const f32x4 l2 = *(const f32x4 *)&sm.lse2[rg * 8 + half * 4];
-            const f32x4 dl = *(const f32x4 *)&sm.delta[rg * 8 + half * 4];
+            for (int rg = 0; rg < 4; ++rg) {
+                const int q0 = rg * 8 + half * 4;
+                const f32x4 st01 = stat[q0 / 2], st23 = stat[q0 / 2 + 1];
+                const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
+                const float dl[4] = {st01[1], st01[3], st23[1], st23[3]};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = rg * 4 + i;
-                float p = fast_exp2(s[r] * scale_log2 - l2[i]);
-                if (!full) {
-                    const int tq = (int)fdiv((uint32_t)(vq0 + acc_row(r, half)), fg);
-                    if (!(key <= tq && tq < my_kend)) p = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rg * 4 + i;
+                    float p = fast_exp2(s[r] * scale_log2 - l2[i]);
+                    if constexpr (decltype(masked)::value) {
+                        const int tq = (int)fdiv((uint32_t)(vq0 + q0 + i), fg);
+                        p = (key <= tq && tq < my_kend) ? p : 0.f;
+                    }
+                    pf[r >> 3][r & 7] = (bf16)p;
+                    dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dl[i]));
                 }
-                const float ds = p * (dp[r] - dl[i]);
-                pf[r >> 3][r & 7] = (bf16)p;
-                dsf[r >> 3][r & 7] = (bf16)ds;
             }
-        }
+        };
+        if (full)
+            softmax(std::false_type{});
+        else
+            softmax(std::true_type{});
+
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const bf16x8 a = *(const bf16x8 *)&sm.dot[db * 32 + col][s2 * 16 + half * 8];
+                const int off = S::T::off(db * 32 + col, 2 * s2 + half);
+                const bf16x8 a = *(const bf16x8 *)(base + S::kDOT + off);
+                const bf16x8 b = *(const bf16x8 *)(base + S::kQT + off);
                 dvacc[db] = mfma32(a, pf[s2], dvacc[db]);
-                const bf16x8 b = *(const bf16x8 *)&sm.qt[db * 32 + col][s2 * 16 + half * 8];
                 dkacc[db] = mfma32(b, dsf[s2], dkacc[db]);
             }
     }
 
     if (!key_ok) return;
-    const size_t base = ((size_t)key * hkv + kh) * D;
+    const size_t obase = ((size_t)key * hkv + kh) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -219,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
                     a[i] = dkacc[db][rg * 4 + i] * scale;
                     b[i] = dvacc[db][rg * 4 + i];
                 }
-                *(f32x4 *)((float *)dk + base + e) = a;
-                *(f32x4 *)((float *)dv + base + e) = b;
+                *(f32x4 *)((float *)dk + obase + e) = a;
+                *(f32x4 *)((float *)dv + obase + e) = b;
             } else {
                 bf16x4 a, b;
 #pragma unroll
@@ -228,8 +244,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
                     a[i] = (bf16)(dkacc[db][rg * 4 + i] * scale);
                     b[i] = (bf16)dvacc[db][rg * 4 + i];
                 }
-                *(bf16x4 *)((bf16 *)dk + base + e) = a;
-                *(bf16x4 *)((bf16 *)dv + base + e) = b;
+                *(bf16x4 *)((bf16 *)dk + obase + e) = a;
+                *(bf16x4 *)((bf16 *)dv + obase + e) = b;
             }
         }
 }
@@ -238,21 +254,24 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
 // dQ
 // ---------------------------------------------------------------------------
 template <int D>
-struct DqTiles {
-    bf16 k[BN][D + 8];
-    bf16 v[BN][D + 8];
-    bf16 kt[D][BN + 8];
+struct DqSmem {
+    using R = SwzTile<BN, D / 8>;    // K or V rows
+    using T = SwzTile<D, BN / 8>;    // K^T (features x keys, perm16 order)
+    static constexpr int kK = 0, kV = R::kBytes, kKT = 2 * R::kBytes;
+    static constexpr int kStage = 2 * R::kBytes + T::kBytes;
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ d_o, const bf16 *__restrict__ kt, const float *__restrict__ lse,
-    const float *__restrict__ delta, const int32_t *__restrict__ kstart, void *__restrict__ dq,
-    int N, int Npad, int hq, int hkv, int g, FastDiv fg, float scale_log2, float scale,
-    int n_row_tiles, int out_f32) {
-    __shared__ DqTiles<D> sm;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bf16 *__restrict__ d_o, const bf16 *__restrict__ kt,
+    const float2 *__restrict__ rowstat, const int32_t *__restrict__ kstart,
+    void *__restrict__ dq, int N, int Npad, int Mpad, int hq, int hkv, int g, FastDiv fg,
+    float scale_log2, float scale, int n_row_tiles, int out_f32) {
+    using S = DqSmem<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int kh = blockIdx.x % hkv;
     const int tile = n_row_tiles - 1 - blockIdx.x / hkv;
@@ -268,9 +287,22 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
     const int key_lo = kstart[t_first];
     const int ks_max = kstart[t_last];
     const int my_ks = kstart[t];
-    const float l2 = lse[(size_t)h * N + t] * SP_LOG2E;
-    const float dl = delta[(size_t)h * N + t];
 
+    const int jt0 = key_lo / BN, jt1 = t_last / BN;
+    // Keys past the end are read from the last key: finite values, always masked.
+    auto stage = [&](int jt, int buf) {
+        char *base = smem + buf * S::kStage;
+        const int j0 = jt * BN;
+        const size_t roff = ((size_t)j0 * hkv + kh) * D;
+        stage_rows_async<BN, D / 8, kWaves>(base + S::kK, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
+        stage_rows_async<BN, D / 8, kWaves>(base + S::kV, wave, lane, v + roff, (size_t)hkv * D * 2, N - j0);
+        stage_rows_async<D, BN / 8, kWaves>(base + S::kKT, wave, lane, kt + (size_t)kh * D * Npad + j0,
+                                            (size_t)Npad * 2, D);
+    };
+    stage(jt0, 0);
+
+    const float2 st2 = rowstat[(size_t)kh * Mpad + vr];
+    const float l2 = st2.x, dl = st2.y;
     bf16x8 qf[D / 16], dof[D / 16];
     {
         const size_t off = ((size_t)t * hq + h) * D + half * 8;
@@ -286,33 +318,12 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[i][r] = 0.f;
 
-    constexpr int KV = BN * D / 8 / kThreads;
-    const int jt0 = key_lo / BN, jt1 = t_last / BN;
     for (int jt = jt0; jt <= jt1; ++jt) {
         const int j0 = jt * BN;
+        wait_async();
         __syncthreads();
-#pragma unroll
-        for (int i = 0; i < KV; ++i) {
-            const int x = tid + i * kThreads;
-            const int r = x / (D / 8), c = x % (D / 8);
-            const int j = j0 + r;
-            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-            if (j < N) {
-                const size_t off = ((size_t)j * hkv + kh) * D + c * 8;
-                a = *(const u32x4 *)(k + off);
-                b = *(const u32x4 *)(v + off);
-            }
-            *(u32x4 *)&sm.k[r][c * 8] = a;
-            *(u32x4 *)&sm.v[r][c * 8] = b;
-        }
-#pragma unroll
-        for (int i = 0; i < KV; ++i) {
-            const int x = tid + i * kThreads;
-            const int e = x / (BN / 8), c = x % (BN / 8);
-            *(u32x4 *)&sm.kt[e][c * 8] =
-                *(const u32x4 *)(kt + ((size_t)kh * D + e) * Npad + j0 + c * 8);
-        }
-        __syncthreads();
+        if (jt < jt1) stage(jt + 1, (jt + 1 - jt0) & 1);
+        const char *base = smem + ((jt - jt0) & 1) * S::kStage;
         const bool full = (j0 + BN - 1 <= t_first) && (j0 >= ks_max);
 
         f32x16 s[2], dp[2];
@@ -322,13 +333,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
             for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
 #pragma unroll
             for (int st = 0; st < D / 16; ++st) {
-                const bf16x8 a = *(const bf16x8 *)&sm.k[kb * 32 + col][16 * st + 8 * half];
-                s[kb] = mfma32(a, qf[st], s[kb]);
-            }
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-                const bf16x8 a = *(const bf16x8 *)&sm.v[kb * 32 + col][16 * st + 8 * half];
-                dp[kb] = mfma32(a, dof[st], dp[kb]);
+                const int off = S::R::off(kb * 32 + col, 2 * st + half);
+                s[kb] = mfma32(*(const bf16x8 *)(base + S::kK + off), qf[st], s[kb]);
+                dp[kb] = mfma32(*(const bf16x8 *)(base + S::kV + off), dof[st], dp[kb]);
             }
         }
         bf16x8 dsf[2][2];
@@ -349,14 +356,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const bf16x8 a =
-                        *(const bf16x8 *)&sm.kt[db * 32 + col][kb * 32 + s2 * 16 + half * 8];
-                    dqacc[db] = mfma32(a, dsf[kb][s2], dqacc[db]);
+                    const int off = S::T::off(db * 32 + col, 4 * kb + 2 * s2 + half);
+                    dqacc[db] = mfma32(*(const bf16x8 *)(base + S::kKT + off), dsf[kb][s2], dqacc[db]);
                 }
     }
 
     if (!row_ok) return;
-    const size_t base = ((size_t)t * hq + h) * D;
+    const size_t obase = ((size_t)t * hq + h) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -366,12 +372,12 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
                 f32x4 a;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) a[i] = dqacc[db][rg * 4 + i] * scale;
-                *(f32x4 *)((float *)dq + base + e) = a;
+                *(f32x4 *)((float *)dq + obase + e) = a;
             } else {
                 bf16x4 a;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) a[i] = (bf16)(dqacc[db][rg * 4 + i] * scale);
-                *(bf16x4 *)((bf16 *)dq + base + e) = a;
+                *(bf16x4 *)((bf16 *)dq + obase + e) = a;
             }
         }
 }
@@ -389,26 +395,39 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     const float scale_log2 = scale * SP_LOG2E;
     hipError_t e;
 
-    const int64_t delta_threads = N * hq * (D / 8);
     {
-        KernelTimer timer("bwd_delta", stream);
-        hipLaunchKernelGGL(k_bwd_delta<D>, dim3((unsigned)((delta_threads + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, (const bf16 *)o, (const bf16 *)d_o, ws.delta,
-                       (int)N, hq);
+        const int64_t threads = (int64_t)hkv * Mpad * (D / 8);
+        KernelTimer timer("bwd_rowstats", stream);
+        hipLaunchKernelGGL(k_bwd_rowstats<D>, dim3((unsigned)((threads + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, (const bf16 *)o, (const bf16 *)d_o, lse,
+                           ws.rowstat, (int)N, hq, hkv, g, fg, (int)Mpad);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_transpose_rows(q, ws.qt, N, hq, hkv, g, D, Mpad, stream)) != hipSuccess) return e;
-    if ((e = launch_transpose_rows(d_o, ws.dot, N, hq, hkv, g, D, Mpad, stream)) != hipSuccess) return e;
-    if ((e = launch_transpose_rows(k, ws.kvt, N, hkv, hkv, 1, D, Npad, stream)) != hipSuccess) return e;
+    // With one KV head the virtual rows of q and dO are their own rows; with
+    // several, row-major virtual-row copies are written next to the transposes.
+    const bool copy_rows = hkv > 1;
+    if ((e = launch_transpose_rows(q, ws.qt, copy_rows ? ws.qv : nullptr, N, hq, hkv, g, D, Mpad,
+                                   stream)) != hipSuccess)
+        return e;
+    if ((e = launch_transpose_rows(d_o, ws.dot, copy_rows ? ws.dov : nullptr, N, hq, hkv, g, D,
+                                   Mpad, stream)) != hipSuccess)
+        return e;
+    if ((e = launch_transpose_rows(k, ws.kvt, nullptr, N, hkv, hkv, 1, D, Npad, stream)) != hipSuccess)
+        return e;
+    const bf16 *qv = copy_rows ? (const bf16 *)ws.qv : (const bf16 *)q;
+    const bf16 *dov = copy_rows ? (const bf16 *)ws.dov : (const bf16 *)d_o;
+    const size_t v_head_stride = copy_rows ? (size_t)Mpad * D : 0;
+    const int v_rows = copy_rows ? (int)Mpad : (int)M;
 
-    const int n_key_tiles = (int)((N + BK - 1) / BK);
     {
+        const int n_key_tiles = (int)((N + BK - 1) / BK);
         KernelTimer timer("attn_bwd_dkdv", stream);
-        hipLaunchKernelGGL(k_attn_bwd_dkdv<D>, dim3((unsigned)(n_key_tiles * hkv)), dim3(kThreads), 0,
-                       stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                       (const bf16 *)d_o, (const bf16 *)ws.qt, (const bf16 *)ws.dot, lse,
-                       (const float *)ws.delta, (const int32_t *)ws.kend, dk, dv, (int)N,
-                       (int)Mpad, hq, hkv, g, fg, scale_log2, scale, (int)grad_f32);
+        hipLaunchKernelGGL(k_attn_bwd_dkdv<D>, dim3((unsigned)(n_key_tiles * hkv)), dim3(kThreads),
+                           0, stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
+                           (const bf16 *)d_o, qv, dov, v_head_stride, v_rows,
+                           (const bf16 *)ws.qt, (const bf16 *)ws.dot,
+                           (const float2 *)ws.rowstat, (const int32_t *)ws.kend, dk, dv, (int)N,
+                           (int)Mpad, hq, hkv, g, fg, scale_log2, scale, (int)grad_f32);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -416,9 +435,9 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     KernelTimer timer("attn_bwd_dq", stream);
     hipLaunchKernelGGL(k_attn_bwd_dq<D>, dim3((unsigned)(n_row_tiles * hkv)), dim3(kThreads), 0,
                        stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                       (const bf16 *)d_o, (const bf16 *)ws.kvt, lse, (const float *)ws.delta,
-                       (const int32_t *)ws.kstart, dq, (int)N, (int)Npad, hq, hkv, g, fg,
-                       scale_log2, scale, n_row_tiles, (int)grad_f32);
+                       (const bf16 *)d_o, (const bf16 *)ws.kvt, (const float2 *)ws.rowstat,
+                       (const int32_t *)ws.kstart, dq, (int)N, (int)Npad, (int)Mpad, hq, hkv, g,
+                       fg, scale_log2, scale, n_row_tiles, (int)grad_f32);
     return hipGetLastError();
 }
 

@@ -20,22 +20,29 @@
 //    (perm16), and the per-row rescale of O is a per-lane multiply.
 //  * fp32 online softmax in the log2 domain (scale * log2(e) folded into one
 //    multiply, exponentials with v_exp_f32).
+//  * K and V^T tiles are double-buffered in LDS (XOR-swizzled, bank-conflict
+//    free) and filled by direct global->LDS loads issued one tile ahead, so
+//    the loads overlap the MFMA and softmax work of the current tile without
+//    occupying registers.
 //  * Tiles inside every row's segment and below every row's diagonal skip
 //    the mask; the key range of a workgroup is [kstart(first row), last row].
 //  * Workgroups are launched longest-first (last row tiles first).
 #include "common.h"
 #include "launch.h"
+#include "tile.h"
 
 namespace {
 
 constexpr int BM = 128;  // virtual query rows per workgroup (4 waves x 32)
 constexpr int BN = 64;   // keys per tile
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
 template <int D>
-struct FwdTiles {
-    bf16 k[BN][D + 8];    // keys x features; +16 B per row keeps the A reads conflict-free
-    bf16 vt[D][BN + 8];   // features x keys (perm16 key order)
+struct FwdSmem {
+    using K = SwzTile<BN, D / 8>;   // keys x features
+    using V = SwzTile<D, BN / 8>;   // features x keys (perm16 key order)
+    static constexpr int kStage = K::kBytes + V::kBytes;
 };
 
 template <int D>
@@ -43,8 +50,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ vt,
     const int32_t *__restrict__ kstart, bf16 *__restrict__ o, float *__restrict__ lse, int N,
     int Npad, int hq, int hkv, int g, FastDiv fg, float scale_log2, int n_row_tiles) {
-    __shared__ FwdTiles<D> sm;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    using S = FwdSmem<D>;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int kh = blockIdx.x % hkv;
     const int tile = n_row_tiles - 1 - blockIdx.x / hkv;
@@ -61,6 +70,18 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(
     const int ks_max = kstart[t_last];
     const int my_ks = kstart[t];
 
+    const int jt0 = key_lo / BN, jt1 = t_last / BN;
+    // Keys past the end are read from the last key: finite values, always masked.
+    auto stage = [&](int jt, int buf) {
+        char *base = smem + buf * S::kStage;
+        const int j0 = jt * BN;
+        stage_rows_async<BN, D / 8, kWaves>(base, wave, lane, k + ((size_t)j0 * hkv + kh) * D,
+                                            (size_t)hkv * D * 2, N - j0);
+        stage_rows_async<D, BN / 8, kWaves>(base + S::K::kBytes, wave, lane,
+                                            vt + (size_t)kh * D * Npad + j0, (size_t)Npad * 2, D);
+    };
+    stage(jt0, 0);
+
     // This lane's query row as the B operand of S^T = K Q^T.
     bf16x8 qf[D / 16];
     {
@@ -76,42 +97,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     float m_run = -1e30f, l_run = 0.f;
 
-    // Register staging of the next tile while the current one is computed.
-    constexpr int KV = BN * D / 8 / kThreads;
-    u32x4 kreg[KV], vreg[KV];
-    auto load_tile = [&](int j0) {
-#pragma unroll
-        for (int i = 0; i < KV; ++i) {
-            const int x = tid + i * kThreads;
-            const int r = x / (D / 8), c = x % (D / 8);
-            const int j = j0 + r;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kreg[i] = j < N ? *(const u32x4 *)(k + ((size_t)j * hkv + kh) * D + c * 8) : z;
-        }
-#pragma unroll
-        for (int i = 0; i < KV; ++i) {
-            const int x = tid + i * kThreads;
-            const int r = x / (BN / 8), c = x % (BN / 8);
-            vreg[i] = *(const u32x4 *)(vt + ((size_t)kh * D + r) * Npad + j0 + c * 8);
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < KV; ++i) {
-            const int x = tid + i * kThreads;
-            *(u32x4 *)&sm.k[x / (D / 8)][(x % (D / 8)) * 8] = kreg[i];
-            *(u32x4 *)&sm.vt[x / (BN / 8)][(x % (BN / 8)) * 8] = vreg[i];
-        }
-    };
-
-    const int jt0 = key_lo / BN, jt1 = t_last / BN;
-    load_tile(jt0 * BN);
     for (int jt = jt0; jt <= jt1; ++jt) {
         const int j0 = jt * BN;
+        wait_async();
         __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (jt < jt1) load_tile(j0 + BN);
+        if (jt < jt1) stage(jt + 1, (jt + 1 - jt0) & 1);
+        const char *ks = smem + ((jt - jt0) & 1) * S::kStage;
+        const char *vs = ks + S::K::kBytes;
         const bool full = (j0 + BN - 1 <= t_first) && (j0 >= ks_max);
 
         f32x16 s[2];
@@ -121,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
             for (int st = 0; st < D / 16; ++st) {
-                const bf16x8 a = *(const bf16x8 *)&sm.k[kb * 32 + col][16 * st + 8 * half];
+                const bf16x8 a = *(const bf16x8 *)(ks + S::K::off(kb * 32 + col, 2 * st + half));
                 s[kb] = mfma32(a, qf[st], s[kb]);
             }
         }
@@ -166,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const bf16x8 a =
-                        *(const bf16x8 *)&sm.vt[db * 32 + col][kb * 32 + s2 * 16 + half * 8];
+                        *(const bf16x8 *)(vs + S::V::off(db * 32 + col, 4 * kb + 2 * s2 + half));
                     oacc[db] = mfma32(a, pf[kb][s2], oacc[db]);
                 }
     }
@@ -197,7 +189,7 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const in
     hipError_t e = launch_segments(pos, ws.kstart, ws.kend, N, stream);
     if (e != hipSuccess) return e;
     const int64_t Npad = (N + 63) / 64 * 64;
-    e = launch_transpose_rows(v, ws.kvt, N, hkv, hkv, 1, d, Npad, stream);
+    e = launch_transpose_rows(v, ws.kvt, nullptr, N, hkv, hkv, 1, d, Npad, stream);
     if (e != hipSuccess) return e;
     const int g = hq / hkv;
     const int M = (int)(N * g);

@@ -24,8 +24,9 @@ class KernelTimer {
 hipError_t launch_relayout(bool to_head, const void *src, void *dst, int P, int64_t N, int G,
                            int H, int d, int rank, hipStream_t stream);
 
-hipError_t launch_transpose_rows(const void *src, void *dst, int64_t N, int heads_src, int n_kv,
-                                 int g, int D, int64_t rows_pad, hipStream_t stream);
+hipError_t launch_transpose_rows(const void *src, void *dst, void *dst_rows, int64_t N,
+                                 int heads_src, int n_kv, int g, int D, int64_t rows_pad,
+                                 hipStream_t stream);
 
 hipError_t launch_segments(const int64_t *pos, int32_t *kstart, int32_t *kend, int64_t N,
                            hipStream_t stream);
@@ -37,7 +38,9 @@ struct AttnWorkspace {
     void *kvt;         // fwd: V^T; bwd: K^T        [hkv][d][Npad]   bf16, keys permuted
     void *qt;          // bwd: Q^T                  [hkv][d][Mpad]   bf16, virtual rows permuted
     void *dot;         // bwd: dO^T                 [hkv][d][Mpad]
-    float *delta;      // bwd: D = rowsum(dO * O)   [hq][N]          fp32
+    void *qv;          // bwd, hkv > 1: Q in virtual-row order  [hkv][Mpad][d]
+    void *dov;         // bwd, hkv > 1: dO in virtual-row order [hkv][Mpad][d]
+    float2 *rowstat;   // bwd: (lse*log2e, rowsum(dO*O)) per virtual row  [hkv][Mpad]
 };
 
 size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws);

@@ -9,6 +9,9 @@
 // each group of 16 positions the order is permuted (perm16) so that the
 // 8 rows a lane feeds one MFMA slot are contiguous (see common.h).
 // Positions past the last row are written as zeros up to `rows_pad`.
+// Optionally the same rows are also written row-major in virtual-row order,
+// [n_kv][rows_pad][D] (zero rows past the end), for kernels that stream
+// row tiles of one KV head's virtual rows.
 #include "common.h"
 #include "launch.h"
 
@@ -19,7 +22,8 @@ constexpr int kRows = 64;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_transpose_rows(const bf16 *__restrict__ src,
-                                                             bf16 *__restrict__ dst, int M,
+                                                             bf16 *__restrict__ dst,
+                                                             bf16 *__restrict__ dst_rows, int M,
                                                              int rows_pad, int heads_src, int g,
                                                              FastDiv fg) {
     __shared__ bf16 tile[kRows][D + 8];
@@ -38,6 +42,7 @@ __global__ __launch_bounds__(kThreads) void k_transpose_rows(const bf16 *__restr
             val = *(const u32x4 *)(src + ((size_t)t * heads_src + hh) * D + c * 8);
         }
         *(u32x4 *)&tile[r][c * 8] = val;
+        if (dst_rows) *(u32x4 *)(dst_rows + ((size_t)kh * rows_pad + v0 + r) * D + c * 8) = val;
     }
     __syncthreads();
 #pragma unroll
@@ -58,9 +63,10 @@ __global__ __launch_bounds__(kThreads) void k_transpose_rows(const bf16 *__restr
 }  // namespace
 
 // src: [N][heads_src][D] bf16; dst: [n_kv][D][rows_pad] bf16 with rows_pad a
-// multiple of 64 and >= N * g.
-hipError_t launch_transpose_rows(const void *src, void *dst, int64_t N, int heads_src, int n_kv,
-                                 int g, int D, int64_t rows_pad, hipStream_t stream) {
+// multiple of 64 and >= N * g; dst_rows: NULL or [n_kv][rows_pad][D] bf16.
+hipError_t launch_transpose_rows(const void *src, void *dst, void *dst_rows, int64_t N,
+                                 int heads_src, int n_kv, int g, int D, int64_t rows_pad,
+                                 hipStream_t stream) {
     const int M = (int)(N * g);
     const dim3 grid((unsigned)(rows_pad / kRows), (unsigned)n_kv);
     if (grid.x == 0) return hipSuccess;
@@ -68,9 +74,11 @@ hipError_t launch_transpose_rows(const void *src, void *dst, int64_t N, int head
     KernelTimer timer("transpose_rows", stream);
     if (D == 128)
         hipLaunchKernelGGL(k_transpose_rows<128>, grid, dim3(kThreads), 0, stream,
-                           (const bf16 *)src, (bf16 *)dst, M, (int)rows_pad, heads_src, g, fg);
+                           (const bf16 *)src, (bf16 *)dst, (bf16 *)dst_rows, M, (int)rows_pad,
+                           heads_src, g, fg);
     else
         hipLaunchKernelGGL(k_transpose_rows<64>, grid, dim3(kThreads), 0, stream,
-                           (const bf16 *)src, (bf16 *)dst, M, (int)rows_pad, heads_src, g, fg);
+                           (const bf16 *)src, (bf16 *)dst, (bf16 *)dst_rows, M, (int)rows_pad,
+                           heads_src, g, fg);
     return hipGetLastError();
 }
