@@ -46,7 +46,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws) {
     const int g = hq / hkv;
-    const int64_t Npad = pad64(N), Mpad = pad64(N * g);
+    const int64_t Mpad = pad64(N * g);
     size_t off = 0;
     char *b = (char *)base;
     auto take = [&](size_t bytes) {
@@ -57,9 +57,6 @@ size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, Attn
     AttnWorkspace w;
     w.kstart = (int32_t *)take(4 * (size_t)N);
     w.kend = (int32_t *)take(4 * (size_t)N);
-    w.kvt = take(2 * (size_t)hkv * d * Npad);
-    w.qt = take(2 * (size_t)hkv * d * Mpad);
-    w.dot = take(2 * (size_t)hkv * d * Mpad);
     w.qv = hkv > 1 ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
     w.dov = hkv > 1 ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
     w.rowstat = (float2 *)take(8 * (size_t)hkv * Mpad);

@@ -13,12 +13,13 @@
 //    32); K and V stay in registers as B operands, and the wave walks the
 //    virtual query rows that can see its keys (t in [j0, segment end)) in
 //    tiles of 32.  S = Q K^T and dP = dO V^T come out with one key per lane,
-//    so P and dS feed dV^T += dO^T P and dK^T += Q^T dS directly (dO^T and
-//    Q^T are pre-transposed copies in perm16 row order).  The GQA sum over
-//    the query heads of a KV head falls out of the virtual-row walk.
+//    so P and dS feed dV^T += dO^T P and dK^T += Q^T dS directly; the dO^T
+//    and Q^T operands are transposing LDS reads of the same Q and dO tiles.
+//    The GQA sum over the query heads of a KV head falls out of the
+//    virtual-row walk.
 //  * k_attn_bwd_dq - a workgroup owns 128 virtual query rows (like the
-//    forward); Q and dO stay in registers, K, V and K^T tiles stream through
-//    LDS, and dQ^T += K^T dS^T accumulates per lane.
+//    forward); Q and dO stay in registers, K and V tiles stream through LDS,
+//    and dQ^T += K^T dS^T accumulates per lane (K^T by transposing reads).
 // Both stream their tiles through double-buffered LDS filled by direct
 // global->LDS loads one tile ahead.  A pre-pass writes, per virtual row,
 // (lse * log2e, D) contiguously, so a row tile's statistics are one load.
@@ -80,18 +81,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
 template <int D>
 struct DkdvSmem {
     using R = SwzTile<BQ, D / 8>;    // Q or dO rows of the tile
-    using T = SwzTile<D, BQ / 8>;    // Q^T or dO^T (features x rows, perm16 order)
-    static constexpr int kQ = 0, kDO = R::kBytes, kQT = 2 * R::kBytes,
-                         kDOT = 2 * R::kBytes + T::kBytes, kStat = 2 * R::kBytes + 2 * T::kBytes;
-    static constexpr int kStage = kStat + 1024;   // (lse2, D) of BQ rows: one wave-wide load
+    static constexpr int kQ = 0, kDO = R::kBytes, kStat = 2 * R::kBytes;
+    static constexpr int kStage = kStat + BQ * 8;   // (lse2, D) of BQ rows
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ d_o, const bf16 *__restrict__ qv, const bf16 *__restrict__ dov,
-    size_t v_head_stride, int v_rows, const bf16 *__restrict__ qt, const bf16 *__restrict__ dot,
-    const float2 *__restrict__ rowstat, const int32_t *__restrict__ kend,
+    size_t v_head_stride, int v_rows, const float2 *__restrict__ rowstat, const int32_t *__restrict__ kend,
     void *__restrict__ dk, void *__restrict__ dv, int N, int Mpad, int hq, int hkv, int g,
     FastDiv fg, float scale_log2, float scale, int out_f32) {
     using S = DkdvSmem<D>;
@@ -124,10 +122,6 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
         const size_t roff = (size_t)kh * v_head_stride + (size_t)vq0 * D;
         stage_rows_async<BQ, D / 8, kWaves>(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
         stage_rows_async<BQ, D / 8, kWaves>(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
-        stage_rows_async<D, BQ / 8, kWaves>(base + S::kQT, wave, lane,
-                                            qt + (size_t)kh * D * Mpad + vq0, (size_t)Mpad * 2, D);
-        stage_rows_async<D, BQ / 8, kWaves>(base + S::kDOT, wave, lane,
-                                            dot + (size_t)kh * D * Mpad + vq0, (size_t)Mpad * 2, D);
         if (wave == kWaves - 1 && lane < BQ * 8 / 16)
             __builtin_amdgcn_global_load_lds(
                 (const void *)((const char *)(rowstat + (size_t)kh * Mpad + vq0) + lane * 16),
@@ -213,9 +207,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const int off = S::T::off(db * 32 + col, 2 * s2 + half);
-                const bf16x8 a = *(const bf16x8 *)(base + S::kDOT + off);
-                const bf16x8 b = *(const bf16x8 *)(base + S::kQT + off);
+                const bf16x8 a = read_tr8<typename S::R>(base + S::kDO, 16 * s2, db * 32, lane);
+                const bf16x8 b = read_tr8<typename S::R>(base + S::kQ, 16 * s2, db * 32, lane);
                 dvacc[db] = mfma32(a, pf[s2], dvacc[db]);
                 dkacc[db] = mfma32(b, dsf[s2], dkacc[db]);
             }
@@ -256,17 +249,16 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
 template <int D>
 struct DqSmem {
     using R = SwzTile<BN, D / 8>;    // K or V rows
-    using T = SwzTile<D, BN / 8>;    // K^T (features x keys, perm16 order)
-    static constexpr int kK = 0, kV = R::kBytes, kKT = 2 * R::kBytes;
-    static constexpr int kStage = 2 * R::kBytes + T::kBytes;
+    static constexpr int kK = 0, kV = R::kBytes;
+    static constexpr int kStage = 2 * R::kBytes;
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
+__global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ d_o, const bf16 *__restrict__ kt,
-    const float2 *__restrict__ rowstat, const int32_t *__restrict__ kstart,
-    void *__restrict__ dq, int N, int Npad, int Mpad, int hq, int hkv, int g, FastDiv fg,
+    const bf16 *__restrict__ d_o, const float2 *__restrict__ rowstat,
+    const int32_t *__restrict__ kstart, void *__restrict__ dq, int N, int Mpad, int hq, int hkv,
+    int g, FastDiv fg,
     float scale_log2, float scale, int n_row_tiles, int out_f32) {
     using S = DqSmem<D>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
@@ -296,8 +288,6 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
         const size_t roff = ((size_t)j0 * hkv + kh) * D;
         stage_rows_async<BN, D / 8, kWaves>(base + S::kK, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
         stage_rows_async<BN, D / 8, kWaves>(base + S::kV, wave, lane, v + roff, (size_t)hkv * D * 2, N - j0);
-        stage_rows_async<D, BN / 8, kWaves>(base + S::kKT, wave, lane, kt + (size_t)kh * D * Npad + j0,
-                                            (size_t)Npad * 2, D);
     };
     stage(jt0, 0);
 
@@ -326,39 +316,43 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dq(
         const char *base = smem + ((jt - jt0) & 1) * S::kStage;
         const bool full = (j0 + BN - 1 <= t_first) && (j0 >= ks_max);
 
-        f32x16 s[2], dp[2];
+        // One 32-key block at a time: S^T and dP^T, then dS^T, then its part
+        // of dQ^T (keeps half the score registers live).
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            f32x16 s, dp;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
             for (int st = 0; st < D / 16; ++st) {
                 const int off = S::R::off(kb * 32 + col, 2 * st + half);
-                s[kb] = mfma32(*(const bf16x8 *)(base + S::kK + off), qf[st], s[kb]);
-                dp[kb] = mfma32(*(const bf16x8 *)(base + S::kV + off), dof[st], dp[kb]);
+                s = mfma32(*(const bf16x8 *)(base + S::kK + off), qf[st], s);
+                dp = mfma32(*(const bf16x8 *)(base + S::kV + off), dof[st], dp);
             }
-        }
-        bf16x8 dsf[2][2];
+            bf16x8 dsf[2];
+            auto grad = [&](auto masked) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(s[kb][r] * scale_log2 - l2);
-                if (!full) {
-                    const int key = j0 + kb * 32 + acc_row(r, half);
-                    if (key < my_ks || key > t) p = 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    float p = fast_exp2(fmaf(s[r], scale_log2, -l2));
+                    if constexpr (decltype(masked)::value) {
+                        const int key = j0 + kb * 32 + acc_row(r, half);
+                        p = (key >= my_ks && key <= t) ? p : 0.f;
+                    }
+                    dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dl));
                 }
-                dsf[kb][r >> 3][r & 7] = (bf16)(p * (dp[kb][r] - dl));
-            }
+            };
+            if (full)
+                grad(std::false_type{});
+            else
+                grad(std::true_type{});
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const int off = S::T::off(db * 32 + col, 4 * kb + 2 * s2 + half);
-                    dqacc[db] = mfma32(*(const bf16x8 *)(base + S::kKT + off), dsf[kb][s2], dqacc[db]);
+                    const bf16x8 a = read_tr8<typename S::R>(base + S::kK, kb * 32 + 16 * s2, db * 32, lane);
+                    dqacc[db] = mfma32(a, dsf[s2], dqacc[db]);
                 }
+        }
     }
 
     if (!row_ok) return;
@@ -389,7 +383,6 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
                       hipStream_t stream) {
     const int g = hq / hkv;
     const int64_t M = N * g;
-    const int64_t Npad = (N + 63) / 64 * 64;
     const int64_t Mpad = (M + 63) / 64 * 64;
     const FastDiv fg = make_fastdiv((uint32_t)g);
     const float scale_log2 = scale * SP_LOG2E;
@@ -404,16 +397,12 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // With one KV head the virtual rows of q and dO are their own rows; with
-    // several, row-major virtual-row copies are written next to the transposes.
+    // several, row-major virtual-row copies are gathered first.
     const bool copy_rows = hkv > 1;
-    if ((e = launch_transpose_rows(q, ws.qt, copy_rows ? ws.qv : nullptr, N, hq, hkv, g, D, Mpad,
-                                   stream)) != hipSuccess)
-        return e;
-    if ((e = launch_transpose_rows(d_o, ws.dot, copy_rows ? ws.dov : nullptr, N, hq, hkv, g, D,
-                                   Mpad, stream)) != hipSuccess)
-        return e;
-    if ((e = launch_transpose_rows(k, ws.kvt, nullptr, N, hkv, hkv, 1, D, Npad, stream)) != hipSuccess)
-        return e;
+    if (copy_rows) {
+        if ((e = launch_gather_rows(q, ws.qv, N, hq, hkv, g, D, Mpad, stream)) != hipSuccess) return e;
+        if ((e = launch_gather_rows(d_o, ws.dov, N, hq, hkv, g, D, Mpad, stream)) != hipSuccess) return e;
+    }
     const bf16 *qv = copy_rows ? (const bf16 *)ws.qv : (const bf16 *)q;
     const bf16 *dov = copy_rows ? (const bf16 *)ws.dov : (const bf16 *)d_o;
     const size_t v_head_stride = copy_rows ? (size_t)Mpad * D : 0;
@@ -425,7 +414,6 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
         hipLaunchKernelGGL(k_attn_bwd_dkdv<D>, dim3((unsigned)(n_key_tiles * hkv)), dim3(kThreads),
                            0, stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
                            (const bf16 *)d_o, qv, dov, v_head_stride, v_rows,
-                           (const bf16 *)ws.qt, (const bf16 *)ws.dot,
                            (const float2 *)ws.rowstat, (const int32_t *)ws.kend, dk, dv, (int)N,
                            (int)Mpad, hq, hkv, g, fg, scale_log2, scale, (int)grad_f32);
     }
@@ -435,9 +423,9 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     KernelTimer timer("attn_bwd_dq", stream);
     hipLaunchKernelGGL(k_attn_bwd_dq<D>, dim3((unsigned)(n_row_tiles * hkv)), dim3(kThreads), 0,
                        stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                       (const bf16 *)d_o, (const bf16 *)ws.kvt, (const float2 *)ws.rowstat,
-                       (const int32_t *)ws.kstart, dq, (int)N, (int)Npad, (int)Mpad, hq, hkv, g,
-                       fg, scale_log2, scale, n_row_tiles, (int)grad_f32);
+                       (const bf16 *)d_o, (const float2 *)ws.rowstat, (const int32_t *)ws.kstart,
+                       dq, (int)N, (int)Mpad, hq, hkv, g, fg, scale_log2, scale, n_row_tiles,
+                       (int)grad_f32);
     return hipGetLastError();
 }
 

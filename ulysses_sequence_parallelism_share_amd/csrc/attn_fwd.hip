@@ -16,17 +16,24 @@
 //    query column: the row max and row sum of the softmax are per-lane
 //    register reductions plus one exchange with lane l^32.
 //  * The probabilities leave the S^T accumulators directly as the B operand
-//    of O^T += V^T P^T; V^T is pre-transposed with the matching key order
-//    (perm16), and the per-row rescale of O is a per-lane multiply.
+//    of O^T += V^T P^T; the V^T operand is read from the natural V tile with
+//    transposing LDS reads (ds_read_b64_tr_b16) in the accumulators' key
+//    order, and the per-row rescale of O is a per-lane multiply.
 //  * fp32 online softmax in the log2 domain (scale * log2(e) folded into one
-//    multiply, exponentials with v_exp_f32).
-//  * K and V^T tiles are double-buffered in LDS (XOR-swizzled, bank-conflict
+//    FMA per score, exponentials with v_exp_f32); the running max is
+//    updated lazily (only when it grows by more than 2^8), so the O
+//    accumulators are rarely rescaled.
+//  * Two workgroups per CU (2 waves per SIMD): one wave's softmax overlaps
+//    the other's MFMAs.
+//  * K and V tiles are double-buffered in LDS (XOR-swizzled, bank-conflict
 //    free) and filled by direct global->LDS loads issued one tile ahead, so
 //    the loads overlap the MFMA and softmax work of the current tile without
 //    occupying registers.
 //  * Tiles inside every row's segment and below every row's diagonal skip
 //    the mask; the key range of a workgroup is [kstart(first row), last row].
 //  * Workgroups are launched longest-first (last row tiles first).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "tile.h"
@@ -40,16 +47,15 @@ constexpr int kWaves = kThreads / 64;
 
 template <int D>
 struct FwdSmem {
-    using K = SwzTile<BN, D / 8>;   // keys x features
-    using V = SwzTile<D, BN / 8>;   // features x keys (perm16 key order)
-    static constexpr int kStage = K::kBytes + V::kBytes;
+    using K = SwzTile<BN, D / 8>;   // keys x features (K and V tiles alike)
+    static constexpr int kStage = 2 * K::kBytes;
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_attn_fwd(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ vt,
+__global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const int32_t *__restrict__ kstart, bf16 *__restrict__ o, float *__restrict__ lse, int N,
-    int Npad, int hq, int hkv, int g, FastDiv fg, float scale_log2, int n_row_tiles) {
+    int hq, int hkv, int g, FastDiv fg, float scale_log2, int n_row_tiles) {
     using S = FwdSmem<D>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -75,10 +81,10 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(
     auto stage = [&](int jt, int buf) {
         char *base = smem + buf * S::kStage;
         const int j0 = jt * BN;
-        stage_rows_async<BN, D / 8, kWaves>(base, wave, lane, k + ((size_t)j0 * hkv + kh) * D,
+        const size_t roff = ((size_t)j0 * hkv + kh) * D;
+        stage_rows_async<BN, D / 8, kWaves>(base, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
+        stage_rows_async<BN, D / 8, kWaves>(base + S::K::kBytes, wave, lane, v + roff,
                                             (size_t)hkv * D * 2, N - j0);
-        stage_rows_async<D, BN / 8, kWaves>(base + S::K::kBytes, wave, lane,
-                                            vt + (size_t)kh * D * Npad + j0, (size_t)Npad * 2, D);
     };
     stage(jt0, 0);
 
@@ -118,35 +124,45 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(
             }
         }
 
-        float mx = -INFINITY;
+        // Row max of the raw scores (masked scores set to -inf), then in the
+        // log2 domain; lanes l and l^32 hold the two halves of one row.
+        auto row_max = [&](auto masked) {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = s[kb][r] * scale_log2;
-                if (!full) {
-                    const int key = j0 + kb * 32 + acc_row(r, half);
-                    if (key < my_ks || key > t) x = -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    if constexpr (decltype(masked)::value) {
+                        const int key = j0 + kb * 32 + acc_row(r, half);
+                        s[kb][r] = (key >= my_ks && key <= t) ? s[kb][r] : -INFINITY;
+                    }
+                    mx = fmaxf(mx, s[kb][r]);
                 }
-                s[kb][r] = x;
-                mx = fmaxf(mx, x);
-            }
-        mx = wave_max_pair(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
+            return mx;
+        };
+        float mx = full ? row_max(std::false_type{}) : row_max(std::true_type{});
+        mx = wave_max_pair(mx) * scale_log2;
+        // Lazy rescaling: the reference max only moves when a row's max
+        // exceeds it by more than 2^8, so the O accumulators are rescaled
+        // rarely; probabilities stay below 256, exact after the final
+        // division by the row sum.
+        if (__any(mx > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i)
+            for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+                for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        }
 
         bf16x8 pf[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(s[kb][r] - m_new);
+                const float p = fast_exp2(fmaf(s[kb][r], scale_log2, -m_run));
                 l_run += p;
                 pf[kb][r >> 3][r & 7] = (bf16)p;
             }
@@ -157,8 +173,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_fwd(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const bf16x8 a =
-                        *(const bf16x8 *)(vs + S::V::off(db * 32 + col, 4 * kb + 2 * s2 + half));
+                    const bf16x8 a = read_tr8<typename S::K>(vs, kb * 32 + 16 * s2, db * 32, lane);
                     oacc[db] = mfma32(a, pf[kb][s2], oacc[db]);
                 }
     }
@@ -188,9 +203,6 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const in
     if (N <= 0) return hipSuccess;
     hipError_t e = launch_segments(pos, ws.kstart, ws.kend, N, stream);
     if (e != hipSuccess) return e;
-    const int64_t Npad = (N + 63) / 64 * 64;
-    e = launch_transpose_rows(v, ws.kvt, nullptr, N, hkv, hkv, 1, d, Npad, stream);
-    if (e != hipSuccess) return e;
     const int g = hq / hkv;
     const int M = (int)(N * g);
     const int n_row_tiles = (M + BM - 1) / BM;
@@ -200,11 +212,11 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const in
     KernelTimer timer("attn_fwd", stream);
     if (d == 128)
         hipLaunchKernelGGL(k_attn_fwd<128>, grid, dim3(kThreads), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, (const bf16 *)ws.kvt, ws.kstart, (bf16 *)o, lse,
-                           (int)N, (int)Npad, hq, hkv, g, fg, scale_log2, n_row_tiles);
+                           (const bf16 *)k, (const bf16 *)v, ws.kstart, (bf16 *)o, lse,
+                           (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles);
     else
         hipLaunchKernelGGL(k_attn_fwd<64>, grid, dim3(kThreads), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, (const bf16 *)ws.kvt, ws.kstart, (bf16 *)o, lse,
-                           (int)N, (int)Npad, hq, hkv, g, fg, scale_log2, n_row_tiles);
+                           (const bf16 *)k, (const bf16 *)v, ws.kstart, (bf16 *)o, lse,
+                           (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles);
     return hipGetLastError();
 }

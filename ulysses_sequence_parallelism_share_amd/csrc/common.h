@@ -58,15 +58,6 @@ __device__ __forceinline__ constexpr int acc_row(int r, int half) {
     return (r >> 2) * 8 + half * 4 + (r & 3);
 }
 
-// The 16 accumulator registers of a 32-row block, taken 8 at a time as the
-// k-slots of a follow-on product, cover rows {16 s + 8 (i/4) + 4 half + i%4}.
-// Storing a transposed operand with positions inside every group of 16
-// permuted by swapping bits 2 and 3 makes those 8 rows one contiguous run
-// at position 16 s + 8 half.  The permutation is its own inverse.
-__device__ __host__ __forceinline__ constexpr int perm16(int x) {
-    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
-}
-
 __device__ __forceinline__ bf16x8 pack8(const f32x16 &a, int base) {
     bf16x8 r;
 #pragma unroll

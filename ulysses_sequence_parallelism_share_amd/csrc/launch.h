@@ -24,9 +24,8 @@ class KernelTimer {
 hipError_t launch_relayout(bool to_head, const void *src, void *dst, int P, int64_t N, int G,
                            int H, int d, int rank, hipStream_t stream);
 
-hipError_t launch_transpose_rows(const void *src, void *dst, void *dst_rows, int64_t N,
-                                 int heads_src, int n_kv, int g, int D, int64_t rows_pad,
-                                 hipStream_t stream);
+hipError_t launch_gather_rows(const void *src, void *dst, int64_t N, int heads_src, int n_kv,
+                              int g, int D, int64_t rows_pad, hipStream_t stream);
 
 hipError_t launch_segments(const int64_t *pos, int32_t *kstart, int32_t *kend, int64_t N,
                            hipStream_t stream);
@@ -35,9 +34,6 @@ hipError_t launch_segments(const int64_t *pos, int32_t *kstart, int32_t *kend, i
 struct AttnWorkspace {
     int32_t *kstart;   // [N]
     int32_t *kend;     // [N]
-    void *kvt;         // fwd: V^T; bwd: K^T        [hkv][d][Npad]   bf16, keys permuted
-    void *qt;          // bwd: Q^T                  [hkv][d][Mpad]   bf16, virtual rows permuted
-    void *dot;         // bwd: dO^T                 [hkv][d][Mpad]
     void *qv;          // bwd, hkv > 1: Q in virtual-row order  [hkv][Mpad][d]
     void *dov;         // bwd, hkv > 1: dO in virtual-row order [hkv][Mpad][d]
     float2 *rowstat;   // bwd: (lse*log2e, rowsum(dO*O)) per virtual row  [hkv][Mpad]
