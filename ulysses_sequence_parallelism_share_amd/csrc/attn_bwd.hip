@@ -9,14 +9,14 @@
 //     dQ = scale dS K,  dK = scale dS^T Q.
 // Two kernels share that recurrence without atomics, so the result is
 // deterministic:
-//  * k_attn_bwd_dkdv - a workgroup owns 128 keys of one KV head (4 waves x
-//    32); K and V stay in registers as B operands, and the wave walks the
-//    virtual query rows that can see its keys (t in [j0, segment end)) in
-//    tiles of 32.  S = Q K^T and dP = dO V^T come out with one key per lane,
-//    so P and dS feed dV^T += dO^T P and dK^T += Q^T dS directly; the dO^T
-//    and Q^T operands are transposing LDS reads of the same Q and dO tiles.
-//    The GQA sum over the query heads of a KV head falls out of the
-//    virtual-row walk.
+//  * k_attn_bwd_dkdv - a workgroup owns 128 keys of one KV head (4 pairs of
+//    waves x 32 keys); K and V stay in registers as B operands, and the
+//    pairs walk the virtual query rows that can see their keys (t in
+//    [j0, segment end)) in tiles of 32.  S = Q K^T and dP = dO V^T come out
+//    with one key per lane, so P and dS feed dV^T += dO^T P and
+//    dK^T += Q^T dS directly; the dO^T and Q^T operands are transposing LDS
+//    reads of the same Q and dO tiles.  The GQA sum over the query heads of
+//    a KV head falls out of the virtual-row walk.
 //  * k_attn_bwd_dq - a workgroup owns 128 virtual query rows (like the
 //    forward); Q and dO stay in registers, K and V tiles stream through LDS,
 //    and dQ^T += K^T dS^T accumulates per lane (K^T by transposing reads).
@@ -77,36 +77,68 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
 
 // ---------------------------------------------------------------------------
 // dK, dV
+//
+// Eight waves: pair p (waves p and p+4) owns keys j0 + 32p .. +31.  Wave p
+// ("A") holds K and accumulates dV: S = Q K^T, P, then dV^T += dO^T P.
+// Wave p+4 ("B") holds V and accumulates dK: dP = dO V^T, then, with P from
+// A, dS = P * (dP - D) and dK^T += Q^T dS.  A hands P to B through LDS in
+// bf16, lane for lane in the accumulator layout both waves share (S and dP
+// are both [rows x keys] products).  Splitting the state keeps each wave
+// under 256 registers, so two waves run per SIMD and one role's softmax
+// overlaps the other's MFMAs.
 // ---------------------------------------------------------------------------
+constexpr int kDkdvThreads = 512;
+constexpr int kDkdvWaves = kDkdvThreads / 64;
+constexpr int kDkdvStages = 4;   // LDS ring: tiles it+1 .. it+3 load while tile it is used
+
 template <int D>
 struct DkdvSmem {
     using R = SwzTile<BQ, D / 8>;    // Q or dO rows of the tile
+    static_assert(R::kInstr <= kDkdvWaves, "at most one Q and one dO load per wave per tile");
+    static_assert(BQ * 8 == kDkdvWaves * 32, "two 16-byte (lse2, D) loads per wave per tile");
     static constexpr int kQ = 0, kDO = R::kBytes, kStat = 2 * R::kBytes;
     static constexpr int kStage = kStat + BQ * 8;   // (lse2, D) of BQ rows
+    static constexpr int kP = kDkdvStages * kStage; // P handed from A to B: [2][pair][lane][16] bf16
+    static constexpr int kPSlot = 4 * 64 * 32;
+    static constexpr int kBytes = kP + 2 * kPSlot;
 };
 
+// Wait until at most `pending` tiles of this wave's direct loads are still
+// in flight; `per_tile` (1 or 3) is how many loads this wave issues per tile.
+__device__ __forceinline__ void wait_tiles(int pending, int per_tile) {
+    switch (pending * per_tile) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;      // vmcnt(0)
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | 1); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F70 | 2); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F70 | 3); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0F70 | 6); break; // 2 tiles x 3 loads
+    }
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ d_o, const bf16 *__restrict__ qv, const bf16 *__restrict__ dov,
-    size_t v_head_stride, int v_rows, const float2 *__restrict__ rowstat, const int32_t *__restrict__ kend,
-    void *__restrict__ dk, void *__restrict__ dv, int N, int Mpad, int hq, int hkv, int g,
+__global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
+    const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ qv,
+    const bf16 *__restrict__ dov, size_t v_head_stride, int v_rows,
+    const float2 *__restrict__ rowstat, const int32_t *__restrict__ kend,
+    void *__restrict__ dk, void *__restrict__ dv, int N, int Mpad, int hkv, int g,
     FastDiv fg, float scale_log2, float scale, int out_f32) {
     using S = DkdvSmem<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
+    __shared__ __attribute__((aligned(1024))) char smem[S::kBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave & 3;
+    const bool role_a = wave < 4;
     const int col = lane & 31, half = lane >> 5;
     const int kh = blockIdx.x % hkv;
     const int j0 = (blockIdx.x / hkv) * BK;
     const int M = N * g;
-    const int key = j0 + wave * 32 + col;
+    const int key = j0 + pair * 32 + col;
     const bool key_ok = key < N;
     const int my_kend = kend[key_ok ? key : N - 1];
-    const int kw0 = j0 + wave * 32;                     // this wave's first key
+    const int kw0 = j0 + pair * 32;                     // the pair's first key
     const int kw1 = min(kw0 + 31, N - 1);               // and last (if kw0 < N)
-    const bool wave_has_keys = kw0 < N;
-    const int kend_w0 = wave_has_keys ? kend[kw0] : 0;
+    const bool pair_has_keys = kw0 < N;
+    const int kend_w0 = pair_has_keys ? kend[kw0] : 0;
     const int kend_max = kend[min(j0 + BK, N) - 1];
 
     // Rows [j0*g, kend_max*g) can see these keys; j0*g is a multiple of BQ.
@@ -120,101 +152,151 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
         char *base = smem + buf * S::kStage;
         const int vq0 = vq_lo + it * BQ;
         const size_t roff = (size_t)kh * v_head_stride + (size_t)vq0 * D;
-        stage_rows_async<BQ, D / 8, kWaves>(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
-        stage_rows_async<BQ, D / 8, kWaves>(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
-        if (wave == kWaves - 1 && lane < BQ * 8 / 16)
+        stage_rows_async<BQ, D / 8, kDkdvWaves>(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
+        stage_rows_async<BQ, D / 8, kDkdvWaves>(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
+        if (lane < 2)   // every wave: two 16-byte pieces of the rows' (lse2, D)
             __builtin_amdgcn_global_load_lds(
-                (const void *)((const char *)(rowstat + (size_t)kh * Mpad + vq0) + lane * 16),
-                (lds_byte *)(base + S::kStat), 16, 0, 0);
+                (const void *)((const char *)(rowstat + (size_t)kh * Mpad + vq0) + wave * 32 + lane * 16),
+                (lds_byte *)(base + S::kStat + wave * 32), 16, 0, 0);
     };
-    if (n_it > 0) stage(0, 0);
+    for (int i = 0; i < kDkdvStages - 1 && i < n_it; ++i) stage(i, i);
 
-    bf16x8 kf[D / 16], vf[D / 16];
+    // This wave's B operand (K for A, V for B), lane = key.
+    bf16x8 kv[D / 16];
     {
+        const bf16 *src = role_a ? k : v;
         const size_t off = ((size_t)(key_ok ? key : 0) * hkv + kh) * D + half * 8;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            bf16x8 a = *(const bf16x8 *)(k + off + 16 * st);
-            bf16x8 b = *(const bf16x8 *)(v + off + 16 * st);
+            bf16x8 a = *(const bf16x8 *)(src + off + 16 * st);
             if (!key_ok) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) a[i] = b[i] = (bf16)0.f;
+                for (int i = 0; i < 8; ++i) a[i] = (bf16)0.f;
             }
-            kf[st] = a;
-            vf[st] = b;
+            kv[st] = a;
         }
     }
-    f32x16 dkacc[D / 32], dvacc[D / 32];
+    f32x16 acc[D / 32];   // dV^T (A) or dK^T (B): lane = key, registers = features
 #pragma unroll
     for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dkacc[i][r] = dvacc[i][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-    for (int it = 0; it < n_it; ++it) {
-        wait_async();
-        __syncthreads();
-        if (it + 1 < n_it) stage(it + 1, (it + 1) & 1);
-        const char *base = smem + (it & 1) * S::kStage;
-        const int vq0 = vq_lo + it * BQ;
-        const int tq_first = (int)fdiv((uint32_t)vq0, fg);
-        const int tq_last = (int)fdiv((uint32_t)(min(vq0 + BQ, M) - 1), fg);
-        // A wave whose pairs are all masked still runs (its P is exactly 0):
-        // that keeps the loop free of divergent exits; it happens only on
-        // the diagonal and at sample ends.
-        const bool full = wave_has_keys && (kw1 <= tq_first) && (tq_last < kend_w0);
-
-        f32x16 s, dp;
+    // A runs one tile ahead of B: in iteration `it`, A turns tile it+1 into P
+    // (double-buffered exchange slot) and dV, while B turns tile it and A's P
+    // of the previous iteration into dS and dK.  One barrier per iteration;
+    // the two roles share no data inside an iteration.  Both roles run the
+    // same MFMA code (only the operand tiles and the middle step differ), so
+    // each accumulator is updated in place.
+    const int rows1 = role_a ? S::kQ : S::kDO;     // rows of the first product (lane = key)
+    const int rows2 = role_a ? S::kDO : S::kQ;     // rows read transposed for the second
+    // Per-lane offsets of the transposing reads of a row tile (k-row base 0;
+    // a k-row base of 16 adds 16 * stride, folded into the read's immediate).
+    int tr_off[D / 32][2];
+    {
+        using R = typename S::R;
+        const int G = lane >> 4, j = lane & 15;
+        const int row = 4 * (G >> 1) + (j >> 2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const int off = S::R::off(col, 2 * st + half);
-            const bf16x8 a = *(const bf16x8 *)(base + S::kQ + off);
-            const bf16x8 b = *(const bf16x8 *)(base + S::kDO + off);
-            s = mfma32(a, kf[st], s);
-            dp = mfma32(b, vf[st], dp);
+        for (int db = 0; db < D / 32; ++db) {
+            const int m = db * 32 + 16 * (G & 1) + 4 * (j & 3);
+            tr_off[db][0] = R::off(row, m >> 3) + (m & 7) * 2;
+            tr_off[db][1] = R::off(row + 8, m >> 3) + (m & 7) * 2;
         }
+    }
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    auto tr_read = [&](const char *tile, int db, int kb) {   // kb: k-row base, multiple of 16
+        const char *p0 = tile + tr_off[db][0] + kb * S::R::kStride;
+        const char *p1 = tile + tr_off[db][1] + kb * S::R::kStride;
+        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds_byte *)p0);
+        const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds_byte *)p1);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    };
+
+    const int per_tile = wave < S::R::kInstr ? 3 : 1;   // direct loads this wave issues per tile
+    if (n_it > 0) wait_tiles(min(kDkdvStages - 2, n_it - 1), per_tile);   // tile 0
+    // Iteration -1 runs A on tile 0 only; iteration it runs A on it+1, B on it.
+    for (int it = -1; it < n_it; ++it) {
+        if (it >= 0) wait_tiles(it + 2 < n_it ? 1 : 0, per_tile);   // tile it+1 for A
+        __syncthreads();
+        if (it >= 0 && it + kDkdvStages - 1 < n_it)
+            stage(it + kDkdvStages - 1, (it + kDkdvStages - 1) % kDkdvStages);
+        const int t = role_a ? it + 1 : it;
+        if (t < 0 || t >= n_it) continue;
+        const char *base = smem + (t % kDkdvStages) * S::kStage;
+        const int vq0 = vq_lo + t * BQ;
+        const f32x4 *stat = (const f32x4 *)(base + S::kStat);   // (lse2, D) of two rows
+        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot + pair * 64 * 32) + lane * 2;
+
+        // First product: S = Q K^T (A) or dP = dO V^T (B); lane = key.
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st)
+            x = mfma32(*(const bf16x8 *)(base + rows1 + S::R::off(col, 2 * st + half)), kv[st], x);
 
         // rows of accumulator register r: rg*8 + half*4 + i (r = rg*4 + i)
-        bf16x8 pf[2], dsf[2];
-        const f32x4 *stat = (const f32x4 *)(base + S::kStat);   // (lse2, D) of two rows
-        auto softmax = [&](auto masked) {
+        bf16x8 opnd[2];
+        if (role_a) {
+            const int tq_first = (int)fdiv((uint32_t)vq0, fg);
+            const int tq_last = (int)fdiv((uint32_t)(min(vq0 + BQ, M) - 1), fg);
+            // A pair whose pairs are all masked still runs (its P is exactly
+            // 0); that happens only on the diagonal and at sample ends.
+            const bool full = pair_has_keys && (kw1 <= tq_first) && (tq_last < kend_w0);
+            auto softmax = [&](auto masked) {
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int q0 = rg * 8 + half * 4;
+                    const f32x4 st01 = stat[q0 / 2], st23 = stat[q0 / 2 + 1];
+                    const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = rg * 4 + i;
+                        float p = fast_exp2(fmaf(x[r], scale_log2, -l2[i]));
+                        if constexpr (decltype(masked)::value) {
+                            const int tq = (int)fdiv((uint32_t)(vq0 + q0 + i), fg);
+                            p = (key <= tq && tq < my_kend) ? p : 0.f;
+                        }
+                        opnd[r >> 3][r & 7] = (bf16)p;
+                    }
+                }
+            };
+            if (full)
+                softmax(std::false_type{});
+            else
+                softmax(std::true_type{});
+            ps[0] = opnd[0];
+            ps[1] = opnd[1];
+        } else {
+            const bf16x8 p0 = ps[0], p1 = ps[1];
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int q0 = rg * 8 + half * 4;
                 const f32x4 st01 = stat[q0 / 2], st23 = stat[q0 / 2 + 1];
-                const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
                 const float dl[4] = {st01[1], st01[3], st23[1], st23[3]};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rg * 4 + i;
-                    float p = fast_exp2(s[r] * scale_log2 - l2[i]);
-                    if constexpr (decltype(masked)::value) {
-                        const int tq = (int)fdiv((uint32_t)(vq0 + q0 + i), fg);
-                        p = (key <= tq && tq < my_kend) ? p : 0.f;
-                    }
-                    pf[r >> 3][r & 7] = (bf16)p;
-                    dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dl[i]));
+                    const float p = (float)(r < 8 ? p0[r] : p1[r - 8]);
+                    opnd[r >> 3][r & 7] = (bf16)(p * (x[r] - dl[i]));
                 }
             }
-        };
-        if (full)
-            softmax(std::false_type{});
-        else
-            softmax(std::true_type{});
+        }
 
+        // Second product: dV^T += dO^T P (A) or dK^T += Q^T dS (B).
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const bf16x8 a = read_tr8<typename S::R>(base + S::kDO, 16 * s2, db * 32, lane);
-                const bf16x8 b = read_tr8<typename S::R>(base + S::kQ, 16 * s2, db * 32, lane);
-                dvacc[db] = mfma32(a, pf[s2], dvacc[db]);
-                dkacc[db] = mfma32(b, dsf[s2], dkacc[db]);
-            }
+            for (int s2 = 0; s2 < 2; ++s2)
+                acc[db] = mfma32(tr_read(base + rows2, db, 16 * s2), opnd[s2], acc[db]);
     }
 
     if (!key_ok) return;
+    void *out = role_a ? dv : dk;
+    const float mul = role_a ? 1.f : scale;
     const size_t obase = ((size_t)key * hkv + kh) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -222,23 +304,15 @@ __global__ __launch_bounds__(kThreads) void k_attn_bwd_dkdv(
         for (int rg = 0; rg < 4; ++rg) {
             const int e = db * 32 + rg * 8 + half * 4;
             if (out_f32) {
-                f32x4 a, b;
+                f32x4 a;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    a[i] = dkacc[db][rg * 4 + i] * scale;
-                    b[i] = dvacc[db][rg * 4 + i];
-                }
-                *(f32x4 *)((float *)dk + obase + e) = a;
-                *(f32x4 *)((float *)dv + obase + e) = b;
+                for (int i = 0; i < 4; ++i) a[i] = acc[db][rg * 4 + i] * mul;
+                *(f32x4 *)((float *)out + obase + e) = a;
             } else {
-                bf16x4 a, b;
+                bf16x4 a;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    a[i] = (bf16)(dkacc[db][rg * 4 + i] * scale);
-                    b[i] = (bf16)dvacc[db][rg * 4 + i];
-                }
-                *(bf16x4 *)((bf16 *)dk + obase + e) = a;
-                *(bf16x4 *)((bf16 *)dv + obase + e) = b;
+                for (int i = 0; i < 4; ++i) a[i] = (bf16)(acc[db][rg * 4 + i] * mul);
+                *(bf16x4 *)((bf16 *)out + obase + e) = a;
             }
         }
 }
@@ -411,11 +485,11 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     {
         const int n_key_tiles = (int)((N + BK - 1) / BK);
         KernelTimer timer("attn_bwd_dkdv", stream);
-        hipLaunchKernelGGL(k_attn_bwd_dkdv<D>, dim3((unsigned)(n_key_tiles * hkv)), dim3(kThreads),
-                           0, stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                           (const bf16 *)d_o, qv, dov, v_head_stride, v_rows,
-                           (const float2 *)ws.rowstat, (const int32_t *)ws.kend, dk, dv, (int)N,
-                           (int)Mpad, hq, hkv, g, fg, scale_log2, scale, (int)grad_f32);
+        hipLaunchKernelGGL(k_attn_bwd_dkdv<D>, dim3((unsigned)(n_key_tiles * hkv)),
+                           dim3(kDkdvThreads), 0, stream, (const bf16 *)k, (const bf16 *)v, qv, dov,
+                           v_head_stride, v_rows, (const float2 *)ws.rowstat,
+                           (const int32_t *)ws.kend, dk, dv, (int)N, (int)Mpad, hkv, g, fg,
+                           scale_log2, scale, (int)grad_f32);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 

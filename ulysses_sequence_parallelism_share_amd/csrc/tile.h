@@ -2,22 +2,25 @@
 //
 // A tile holds ROWS rows of CH 16-byte chunks (CH = 4, 8 or 16), stored
 // densely (row stride CH*16 bytes) with an XOR swizzle: logical chunk c of
-// row r sits at physical chunk c ^ sw(r), with x = (r / RP) % CH (RP = 16/CH
-// rows share one 256-byte line of the 64 LDS banks) and sw(r) = x rotated
-// left by one bit within log2(CH) bits.  Two read patterns are then
-// bank-conflict free:
-//  * 16 bytes per lane, one row per lane (16 consecutive rows, one chunk):
-//    sw is a bijection of x;
-//  * the transposing read (below), where 16 lanes fetch 4 consecutive rows
-//    x 32 bytes (chunks c, c+1 with c even): rotating makes sw of the two
-//    row pairs differ in a bit above bit 0, so the 8 chunks land apart.
+// row r sits at physical chunk c ^ sw(r).  RP = 16/CH rows share one
+// 256-byte line of the 64 LDS banks (16 chunk slots).  Two read patterns
+// must be bank-conflict free:
+//  * 16 bytes per lane, one row per lane, 16 consecutive rows at one chunk
+//    (served 16 lanes at a time): (r % RP, sw(r)) must be distinct over the
+//    16 rows, i.e. sw a bijection of x = (r / RP) % CH;
+//  * the transposing read (below), served 32 lanes at a time: 4 consecutive
+//    rows r0..r0+3 (r0 % 4 == 0) x 64 bytes (chunks c..c+3, c % 4 == 0)
+//    must fill 16 distinct chunk slots, so the sw of rows sharing a line
+//    slot must differ in bit 2 or 3.
+// CH = 16: sw swaps the two 2-bit halves of x = r % 16 (rows r0+z get
+// 4z + const); CH = 8: x = (r/2) % 8, sw = (x % 2) * 4 + x / 2 (rows r0,
+// r0+1 and r0+2, r0+3 differ in bit 2); CH = 4: sw = x.
 //
 // A direct load writes a wave's 64 lanes to 64 consecutive 16-byte LDS
 // slots (base + lane*16): load i of a tile fills rows i*64/CH ... and lane l
-// fetches row i*64/CH + l/CH, logical chunk (l % CH) ^ sw(row); since
-// x = (4i + l/16) % CH and rotation is linear over XOR, that chunk is
-// (l % CH) ^ rot(l/16) ^ rot(4i % CH).  The loads complete asynchronously:
-// wait_async() (vmcnt 0) and a workgroup barrier publish the tile.
+// fetches row i*64/CH + l/CH, logical chunk (l % CH) ^ sw(row).  The loads
+// complete asynchronously: wait_async() (vmcnt 0) and a workgroup barrier
+// publish the tile.
 #pragma once
 
 #include "common.h"
@@ -33,10 +36,10 @@ struct SwzTile {
     static constexpr int kInstr = ROWS * CH / 64;
     static_assert(kInstr * 64 == ROWS * CH, "tile must be whole wave-wide loads");
 
-    __device__ static constexpr int rot(int x) {   // rotate left by 1 within log2(CH) bits
-        return ((x << 1) & (CH - 1)) | (x >> (CH == 16 ? 3 : CH == 8 ? 2 : 1));
+    __device__ static constexpr int swz(int r) {
+        const int x = (r / RP) & (CH - 1);
+        return CH == 16 ? (((x & 3) << 2) | (x >> 2)) : CH == 8 ? (((x & 1) << 2) | (x >> 1)) : x;
     }
-    __device__ static constexpr int swz(int r) { return rot((r / RP) & (CH - 1)); }
     // byte offset of logical chunk c of row r
     __device__ static constexpr int off(int r, int c) { return r * kStride + ((c ^ swz(r)) << 4); }
 };
@@ -50,11 +53,10 @@ __device__ __forceinline__ void stage_rows_async(char *tile, int wave, int lane,
     using T = SwzTile<ROWS, CH>;
     lds_byte *lds = (lds_byte *)tile;   // the tile lives in __shared__ memory
     const char *src = (const char *)base;
-    const int a = (lane & (CH - 1)) ^ T::rot((lane >> 4) & (CH - 1));
     for (int i = wave; i < T::kInstr; i += NWAVES) {
-        int r = i * (64 / CH) + lane / CH;
-        r = r < valid_rows ? r : valid_rows - 1;
-        const int c = a ^ T::rot((4 * i) & (CH - 1));
+        const int rs = i * (64 / CH) + lane / CH;          // LDS row of this slot
+        const int r = rs < valid_rows ? rs : valid_rows - 1; // global row it holds
+        const int c = (lane & (CH - 1)) ^ T::swz(rs);
         __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)r * row_stride + c * 16),
                                          lds + i * 1024, 16, 0, 0);
     }
