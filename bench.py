@@ -105,10 +105,22 @@ def relayout_bound(dev, reps):
     ops.sp_timing_enable(False)
     exact = bool(torch.equal(back.view(torch.int16), x.view(torch.int16)))
     nbytes = 2 * x.numel() * 2                      # read once + write once
-    out = {"workload": w.name, "bytes_per_direction": nbytes, "bit_exact_roundtrip": exact}
+    # reference: a plain device-to-device copy of the same buffer (torch copy_)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    back.copy_(x)
+    torch.cuda.synchronize()
+    s0.record()
+    for _ in range(reps):
+        back.copy_(x)
+    s1.record()
+    torch.cuda.synchronize()
+    copy_ms = s0.elapsed_time(s1) / reps
+    out = {"workload": w.name, "bytes_per_direction": nbytes, "bit_exact_roundtrip": exact,
+           "plain_copy": {"avg_ms": copy_ms, "GB/s": nbytes / copy_ms / 1e6}}
     for key, name in (("seq_to_head", "relayout_seq_to_head"), ("head_to_seq", "relayout_head_to_seq")):
         ms = kt[name]["avg_ms"]
-        out[key] = {"avg_ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm": nbytes / ms / 1e6 / PEAK_HBM_GBPS}
+        out[key] = {"avg_ms": ms, "GB/s": nbytes / ms / 1e6, "frac_hbm": nbytes / ms / 1e6 / PEAK_HBM_GBPS,
+                    "frac_plain_copy": copy_ms / ms}
     del x, h, back
     torch.cuda.empty_cache()
     return out

@@ -510,7 +510,7 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const vo
                            int hq, int hkv, int d, float scale, bool grad_f32, void *dq,
                            void *dk, void *dv, const AttnWorkspace &ws, hipStream_t stream) {
     if (N <= 0) return hipSuccess;
-    hipError_t e = launch_segments(pos, ws.kstart, ws.kend, N, stream);
+    hipError_t e = launch_segments(pos, ws.kstart, ws.kend, ws.seg_agg, N, stream);
     if (e != hipSuccess) return e;
     if (d == 128)
         return bwd_launch<128>(q, k, v, o, d_o, lse, N, hq, hkv, scale, grad_f32, dq, dk, dv, ws,

@@ -201,7 +201,7 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const in
                            int64_t N, int hq, int hkv, int d, float scale, void *o, float *lse,
                            const AttnWorkspace &ws, hipStream_t stream) {
     if (N <= 0) return hipSuccess;
-    hipError_t e = launch_segments(pos, ws.kstart, ws.kend, N, stream);
+    hipError_t e = launch_segments(pos, ws.kstart, ws.kend, ws.seg_agg, N, stream);
     if (e != hipSuccess) return e;
     const int g = hq / hkv;
     const int M = (int)(N * g);

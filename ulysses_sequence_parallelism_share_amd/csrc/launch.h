@@ -27,13 +27,16 @@ hipError_t launch_relayout(bool to_head, const void *src, void *dst, int P, int6
 hipError_t launch_gather_rows(const void *src, void *dst, int64_t N, int heads_src, int n_kv,
                               int g, int D, int64_t rows_pad, hipStream_t stream);
 
-hipError_t launch_segments(const int64_t *pos, int32_t *kstart, int32_t *kend, int64_t N,
-                           hipStream_t stream);
+// Scratch ints the segment pre-pass needs for N tokens (per-chunk aggregates).
+size_t segments_scratch_ints(int64_t N);
+hipError_t launch_segments(const int64_t *pos, int32_t *kstart, int32_t *kend, int32_t *agg,
+                           int64_t N, hipStream_t stream);
 
 // Workspace layout shared by the forward and backward calls.
 struct AttnWorkspace {
     int32_t *kstart;   // [N]
     int32_t *kend;     // [N]
+    int32_t *seg_agg;  // segment pre-pass chunk aggregates
     void *qv;          // bwd, hkv > 1: Q in virtual-row order  [hkv][Mpad][d]
     void *dov;         // bwd, hkv > 1: dO in virtual-row order [hkv][Mpad][d]
     float2 *rowstat;   // bwd: (lse*log2e, rowsum(dO*O)) per virtual row  [hkv][Mpad]
