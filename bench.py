@@ -14,6 +14,7 @@ step (algorithmic FLOPs 14*d*A*hq, A = allowed causal pairs per head).
 from __future__ import annotations
 
 import argparse
+import re
 import json
 import os
 import sys
@@ -44,6 +45,11 @@ def parse():
                     help="timed round trips of the relayout-bound workload (0: skip)")
     ap.add_argument("--cpu-tokens", type=int, default=20480,
                     help="tokens of the oracle's CPU-baseline sample (0: skip)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="print a text summary of a rocprofv3 --stats kernel table and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM-traffic summary of two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, then WRITE_SIZE) and exit")
     return ap.parse_args()
 
 
@@ -79,6 +85,122 @@ def cpu_baseline(w, tokens):
             "sample": f"fp64 oracle attn_fwd+attn_bwd on one causal sample of {L} tokens "
                       f"(the first {L} tokens of the workload's first packed sample), "
                       f"hq={w.hq}, hkv={w.hkv}, d={w.head_dim}; {flops:.3e} algorithmic FLOP"}
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the attention kernels, from rocprofv3 counters.
+#
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one --pmc run each) are scaled
+# by what the same counter reads for a plain device copy of known size in the
+# same run (the relayout-bound workload's copy_ of 6 GiB), so that the figure
+# is in bytes of HBM traffic.  The summary records a hash of the sources each
+# kernel is built from; the bench reports the traffic only while it matches.
+# ---------------------------------------------------------------------------
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_500k_share_hbm_traffic.txt")
+KERNEL_SYMBOL = {"attn_fwd": "k_attn_fwd", "attn_bwd_dkdv": "k_attn_bwd_dkdv",
+                 "attn_bwd_dq": "k_attn_bwd_dq"}
+KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "attn_bwd_dkdv": "attn_bwd.hip",
+                  "attn_bwd_dq": "attn_bwd.hip"}
+
+
+def sources_hash(kernel):
+    import hashlib
+    csrc = os.path.join(ROOT, "ulysses_sequence_parallelism_share_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (os.path.join(csrc, KERNEL_SOURCES[kernel]), os.path.join(csrc, "common.h"),
+              os.path.join(csrc, "tile.h"), os.path.join(csrc, "launch.h"),
+              os.path.join(ROOT, "ulysses_sequence_parallelism_share_amd", "build.py")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter_csv(path, counter):
+    """Per-dispatch values of one counter: list of (kernel_name, KiB)."""
+    import csv
+    acc = {}
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            key = int(row["Dispatch_Id"])
+            name, val = acc.get(key, (row["Kernel_Name"], 0.0))
+            acc[key] = (name, val + float(row["Counter_Value"]))
+    return [acc[k] for k in sorted(acc)]
+
+
+def summarize_traffic(fetch_csv, write_csv):
+    from synth import configs
+    w = configs.WORKLOADS[4]
+    copy_bytes = 2 * w.n_tokens * w.relayout_groups * w.relayout_heads * w.head_dim
+    out = ["# HBM traffic per dispatch from rocprofv3 counters, 500K-token rank share",
+           "# (N=524288, hq=4, hkv=1, d=128, 4 packed samples)",
+           "# commands (GPU, from /tmp with TMPDIR=/tmp; REPO = the repository root):",
+           "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d REPO/gpurun_out/pmc_fetch -o run "
+           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0",
+           "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d REPO/gpurun_out/pmc_write -o run "
+           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0",
+           "#   python3 REPO/bench.py --summarize-traffic "
+           "REPO/gpurun_out/pmc_fetch/run_counter_collection.csv "
+           "REPO/gpurun_out/pmc_write/run_counter_collection.csv",
+           f"# calibration: the largest dispatch whose name holds 'copy' is the plain copy of "
+           f"{copy_bytes} bytes (read {copy_bytes} + write {copy_bytes})"]
+    factors = {}
+    per_kernel = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = read_counter_csv(path, counter)
+        copies = [v for n, v in rows if "copy" in n.lower()]
+        if not copies:
+            raise SystemExit(f"{path}: no copy dispatch to calibrate {counter} against")
+        cal = max(copies)
+        factors[counter] = copy_bytes / (cal * 1024.0)
+        out.append(f"# {counter}: copy reads {cal:.1f} KiB -> factor {factors[counter]:.4f} "
+                   "(bytes per counted byte)")
+        for kernel, sym in KERNEL_SYMBOL.items():
+            pat = re.compile(r"(^|[\s:])" + sym + r"[<(]")
+            vals = [v for n, v in rows if pat.search(n)]
+            if vals:
+                per_kernel.setdefault(kernel, {})[counter] = (sum(vals) / len(vals), len(vals))
+    out.append("# per dispatch: counter KiB as read; traffic_bytes = fetch*1024*f_fetch + "
+               "write*1024*f_write")
+    for kernel, c in per_kernel.items():
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        fk, nd = c["FETCH_SIZE"]
+        wk, _ = c["WRITE_SIZE"]
+        tb = fk * 1024 * factors["FETCH_SIZE"] + wk * 1024 * factors["WRITE_SIZE"]
+        out.append(f"kernel={kernel} dispatches={nd} fetch_kib={fk:.1f} write_kib={wk:.1f} "
+                   f"traffic_bytes={tb:.0f} sources={sources_hash(kernel)}")
+    return "\n".join(out)
+
+
+def load_traffic(kernel):
+    """Traffic bytes per launch of `kernel` from the committed summary, or None when the
+    summary is absent or was taken from other sources than the current ones."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            lines = fh.read().splitlines()
+    except OSError:
+        return None
+    for ln in lines:
+        if not ln.startswith("kernel="):
+            continue
+        kv = dict(tok.split("=", 1) for tok in ln.split())
+        if kv["kernel"] == kernel and kv["sources"] == sources_hash(kernel):
+            return float(kv["traffic_bytes"])
+    return None
+
+
+def summarize_trace(stats_csv):
+    import csv
+    rows = []
+    with open(stats_csv, newline="") as fh:
+        for r in csv.DictReader(fh):
+            rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3,
+                         float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
+    out = [f"{'kernel':<44}{'calls':>7}{'total_us':>15}{'avg_us':>13}{'pct':>9}"]
+    for n, c, t, a, p in rows:
+        out.append(f"{n[:42]:<44}{c:>7}{t:>15.1f}{a:>13.1f}{p:>8.2f}%")
+    return "\n".join(out)
 
 
 def relayout_bound(dev, reps):
@@ -128,6 +250,12 @@ def relayout_bound(dev, reps):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the all-to-all is emulated on one device); run with --gpus 1.", file=sys.stderr)
@@ -229,13 +357,14 @@ def main():
     dkdv_ms = kt["attn_bwd_dkdv"]["avg_ms"]
     dq_ms = kt["attn_bwd_dq"]["avg_ms"]
     attn_kernel_ms = sum(per_step.get(n, 0.0) for n in
-                         ("segments", "transpose_rows", "attn_fwd", "bwd_delta", "attn_bwd_dkdv",
-                          "attn_bwd_dq"))
+                         ("segment_chunks", "segment_scan", "gather_rows", "attn_fwd",
+                          "bwd_rowstats", "attn_bwd_dkdv", "attn_bwd_dq"))
     algo = {"attn_fwd": fwd_flop, "attn_bwd_dkdv": 0.8 * bwd_flop, "attn_bwd_dq": 0.2 * bwd_flop}
     dom = max(algo, key=lambda n: kt[n]["avg_ms"])
     dom_tflops = algo[dom] / kt[dom]["avg_ms"] / 1e9
     roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
+                "traffic": load_traffic(dom) if args.workload == 5 else None,
                 "avg_ms": kt[dom]["avg_ms"], "algorithmic_flop_per_launch": algo[dom]}
     value = (fwd_flop + bwd_flop) / ms_per_step / 1e9
     attention = {
