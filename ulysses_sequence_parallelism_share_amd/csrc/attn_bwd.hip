@@ -12,9 +12,9 @@
 //  * k_attn_bwd_dkdv - a workgroup owns 128 keys of one KV head (4 pairs of
 //    waves x 32 keys); K and V stay in registers as B operands, and the
 //    pairs walk the virtual query rows that can see their keys (t in
-//    [j0, segment end)) in tiles of 32.  S = Q K^T and dP = dO V^T come out
-//    with one key per lane, so P and dS feed dV^T += dO^T P and
-//    dK^T += Q^T dS directly; the dO^T and Q^T operands are transposing LDS
+//    [j0, segment end)) in tiles of 32, from the segment end down.
+//    S = Q K^T and dP = dO V^T come out with one key per lane, so P and dS
+//    feed dV^T += dO^T P and dK^T += Q^T dS directly; the dO^T and Q^T operands are transposing LDS
 //    reads of the same Q and dO tiles.  The GQA sum over the query heads of
 //    a KV head falls out of the virtual-row walk.
 //  * k_attn_bwd_dq - a workgroup owns 128 virtual query rows (like the
@@ -144,13 +144,17 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
     // Rows [j0*g, kend_max*g) can see these keys; j0*g is a multiple of BQ.
     const int vq_lo = j0 * g;
     const int n_it = (kend_max * g - vq_lo + BQ - 1) / BQ;
+    // Tiles are walked from the end of the range down to the diagonal: key
+    // tiles of one sample share that end, so workgroups running side by side
+    // read the same Q and dO rows at about the same time and share them in L2.
+    auto tile_row = [&](int it) { return vq_lo + (n_it - 1 - it) * BQ; };
     // Q and dO rows come from virtual-row-major copies (row v of KV head kh at
     // qv + kh*v_head_stride + v*D; `v_rows` rows exist).  Rows past the end
     // are read from the last row: finite data, and their statistics make P
     // exactly 0.
     auto stage = [&](int it, int buf) {
         char *base = smem + buf * S::kStage;
-        const int vq0 = vq_lo + it * BQ;
+        const int vq0 = tile_row(it);
         const size_t roff = (size_t)kh * v_head_stride + (size_t)vq0 * D;
         stage_rows_async<BQ, D / 8, kDkdvWaves>(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
         stage_rows_async<BQ, D / 8, kDkdvWaves>(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
         const int t = role_a ? it + 1 : it;
         if (t < 0 || t >= n_it) continue;
         const char *base = smem + (t % kDkdvStages) * S::kStage;
-        const int vq0 = vq_lo + t * BQ;
+        const int vq0 = tile_row(t);
         const f32x4 *stat = (const f32x4 *)(base + S::kStat);   // (lse2, D) of two rows
         bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot + pair * 64 * 32) + lane * 2;
 
