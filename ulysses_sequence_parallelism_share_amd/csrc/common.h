@@ -1,6 +1,6 @@
 // Shared device-side definitions for the gfx950 kernels of the Ulysses
-// attention share: vector types, MFMA wrappers, fast division by run-time
-// constants and the key-order permutation used by the transposed tiles.
+// attention share: vector types, the MFMA wrapper and its accumulator
+// layout, and fast division by run-time constants.
 #pragma once
 
 #include <hip/hip_runtime.h>
