@@ -109,8 +109,15 @@ def sources_hash(kernel):
     for f in (os.path.join(csrc, KERNEL_SOURCES[kernel]), os.path.join(csrc, "common.h"),
               os.path.join(csrc, "tile.h"), os.path.join(csrc, "launch.h"),
               os.path.join(ROOT, "ulysses_sequence_parallelism_share_amd", "build.py")):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            text = fh.read()
+        # code only: comments and layout do not change the kernel
+        if f.endswith(".py"):
+            text = re.sub(r"#[^\n]*", "", text)
+        else:
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
