@@ -152,12 +152,14 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
     // qv + kh*v_head_stride + v*D; `v_rows` rows exist).  Rows past the end
     // are read from the last row: finite data, and their statistics make P
     // exactly 0.
+    RowStager<BQ, D / 8, kDkdvWaves> stager;
+    stager.init(wave, lane, D * 2);
     auto stage = [&](int it, int buf) {
         char *base = smem + buf * S::kStage;
         const int vq0 = tile_row(it);
         const size_t roff = (size_t)kh * v_head_stride + (size_t)vq0 * D;
-        stage_rows_async<BQ, D / 8, kDkdvWaves>(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
-        stage_rows_async<BQ, D / 8, kDkdvWaves>(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
+        stager.issue(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
+        stager.issue(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
         if (lane < 2)   // every wave: two 16-byte pieces of the rows' (lse2, D)
             __builtin_amdgcn_global_load_lds(
                 (const void *)((const char *)(rowstat + (size_t)kh * Mpad + vq0) + wave * 32 + lane * 16),
@@ -360,12 +362,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
 
     const int jt0 = key_lo / BN, jt1 = t_last / BN;
     // Keys past the end are read from the last key: finite values, always masked.
+    RowStager<BN, D / 8, kWaves> stager;
+    stager.init(wave, lane, (uint32_t)(hkv * D * 2));
     auto stage = [&](int jt, int buf) {
         char *base = smem + buf * S::kStage;
         const int j0 = jt * BN;
         const size_t roff = ((size_t)j0 * hkv + kh) * D;
-        stage_rows_async<BN, D / 8, kWaves>(base + S::kK, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
-        stage_rows_async<BN, D / 8, kWaves>(base + S::kV, wave, lane, v + roff, (size_t)hkv * D * 2, N - j0);
+        stager.issue(base + S::kK, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
+        stager.issue(base + S::kV, wave, lane, v + roff, (size_t)hkv * D * 2, N - j0);
     };
     stage(jt0, 0);
 
@@ -386,13 +390,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[i][r] = 0.f;
 
-    for (int jt = jt0; jt <= jt1; ++jt) {
+    // One key tile; `masked` selects the code that evaluates the mask.
+    auto tile_step = [&](int jt, auto masked) {
         const int j0 = jt * BN;
         wait_async();
         __syncthreads();
         if (jt < jt1) stage(jt + 1, (jt + 1 - jt0) & 1);
         const char *base = smem + ((jt - jt0) & 1) * S::kStage;
-        const bool full = (j0 + BN - 1 <= t_first) && (j0 >= ks_max);
 
         // One 32-key block at a time: S^T and dP^T, then dS^T, then its part
         // of dQ^T (keeps half the score registers live).
@@ -408,21 +412,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
                 dp = mfma32(*(const bf16x8 *)(base + S::kV + off), dof[st], dp);
             }
             bf16x8 dsf[2];
-            auto grad = [&](auto masked) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float p = fast_exp2(fmaf(s[r], scale_log2, -l2));
-                    if constexpr (decltype(masked)::value) {
-                        const int key = j0 + kb * 32 + acc_row(r, half);
-                        p = (key >= my_ks && key <= t) ? p : 0.f;
-                    }
-                    dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dl));
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(s[r], scale_log2, -l2));
+                if constexpr (decltype(masked)::value) {
+                    const int key = j0 + kb * 32 + acc_row(r, half);
+                    p = (key >= my_ks && key <= t) ? p : 0.f;
                 }
-            };
-            if (full)
-                grad(std::false_type{});
-            else
-                grad(std::true_type{});
+                dsf[r >> 3][r & 7] = (bf16)(p * (dp[r] - dl));
+            }
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -431,7 +429,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
                     dqacc[db] = mfma32(a, dsf[s2], dqacc[db]);
                 }
         }
-    }
+    };
+
+    // Tiles [fa, fb] lie inside every row's segment and below every row's
+    // diagonal and skip the mask (separate loops keep the mask code out of
+    // them entirely).
+    const int fa = max(jt0, (ks_max + BN - 1) / BN);
+    const int fb = min(jt1, t_first >= BN - 1 ? (t_first - (BN - 1)) / BN : -1);
+    int jt = jt0;
+    for (; jt <= jt1 && jt < fa; ++jt) tile_step(jt, std::true_type{});
+    for (; jt <= fb; ++jt) tile_step(jt, std::false_type{});
+    for (; jt <= jt1; ++jt) tile_step(jt, std::true_type{});
 
     if (!row_ok) return;
     const size_t obase = ((size_t)t * hq + h) * D;

@@ -78,13 +78,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
 
     const int jt0 = key_lo / BN, jt1 = t_last / BN;
     // Keys past the end are read from the last key: finite values, always masked.
+    RowStager<BN, D / 8, kWaves> stager;
+    stager.init(wave, lane, (uint32_t)(hkv * D * 2));
     auto stage = [&](int jt, int buf) {
         char *base = smem + buf * S::kStage;
         const int j0 = jt * BN;
         const size_t roff = ((size_t)j0 * hkv + kh) * D;
-        stage_rows_async<BN, D / 8, kWaves>(base, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
-        stage_rows_async<BN, D / 8, kWaves>(base + S::K::kBytes, wave, lane, v + roff,
-                                            (size_t)hkv * D * 2, N - j0);
+        stager.issue(base, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
+        stager.issue(base + S::K::kBytes, wave, lane, v + roff, (size_t)hkv * D * 2, N - j0);
     };
     stage(jt0, 0);
 
@@ -103,14 +104,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     float m_run = -1e30f, l_run = 0.f;
 
-    for (int jt = jt0; jt <= jt1; ++jt) {
+    // One key tile; `masked` selects the code that evaluates the mask.
+    auto tile_step = [&](int jt, auto masked) {
         const int j0 = jt * BN;
         wait_async();
         __syncthreads();
         if (jt < jt1) stage(jt + 1, (jt + 1 - jt0) & 1);
         const char *ks = smem + ((jt - jt0) & 1) * S::kStage;
         const char *vs = ks + S::K::kBytes;
-        const bool full = (j0 + BN - 1 <= t_first) && (j0 >= ks_max);
 
         f32x16 s[2];
 #pragma unroll
@@ -126,21 +127,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
 
         // Row max of the raw scores (masked scores set to -inf), then in the
         // log2 domain; lanes l and l^32 hold the two halves of one row.
-        auto row_max = [&](auto masked) {
-            float mx = -INFINITY;
+        float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    if constexpr (decltype(masked)::value) {
-                        const int key = j0 + kb * 32 + acc_row(r, half);
-                        s[kb][r] = (key >= my_ks && key <= t) ? s[kb][r] : -INFINITY;
-                    }
-                    mx = fmaxf(mx, s[kb][r]);
+            for (int r = 0; r < 16; ++r) {
+                if constexpr (decltype(masked)::value) {
+                    const int key = j0 + kb * 32 + acc_row(r, half);
+                    s[kb][r] = (key >= my_ks && key <= t) ? s[kb][r] : -INFINITY;
                 }
-            return mx;
-        };
-        float mx = full ? row_max(std::false_type{}) : row_max(std::true_type{});
+                mx = fmaxf(mx, s[kb][r]);
+            }
         mx = wave_max_pair(mx) * scale_log2;
         // Lazy rescaling: the reference max only moves when a row's max
         // exceeds it by more than 2^8, so the O accumulators are rescaled
@@ -176,7 +173,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
                     const bf16x8 a = read_tr8<typename S::K>(vs, kb * 32 + 16 * s2, db * 32, lane);
                     oacc[db] = mfma32(a, pf[kb][s2], oacc[db]);
                 }
-    }
+    };
+
+    // Tiles [fa, fb] lie inside every row's segment and below every row's
+    // diagonal and skip the mask; the tiles before and after evaluate it.
+    // Separate loops keep the mask code out of the unmasked tiles entirely.
+    const int fa = max(jt0, (ks_max + BN - 1) / BN);
+    const int fb = min(jt1, t_first >= BN - 1 ? (t_first - (BN - 1)) / BN : -1);
+    int jt = jt0;
+    for (; jt <= jt1 && jt < fa; ++jt) tile_step(jt, std::true_type{});
+    for (; jt <= fb; ++jt) tile_step(jt, std::false_type{});
+    for (; jt <= jt1; ++jt) tile_step(jt, std::true_type{});
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.f / l_tot;

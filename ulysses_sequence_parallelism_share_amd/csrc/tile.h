@@ -62,6 +62,41 @@ __device__ __forceinline__ void stage_rows_async(char *tile, int wave, int lane,
     }
 }
 
+// The same loads with the per-lane part of each address computed once: a
+// wave keeps, for each load it issues, its lane's byte offset within the
+// source tile, so staging a full tile costs one address add per load.  Only
+// a tile with fewer than ROWS valid rows (the last one) takes the clamping
+// path above.
+template <int ROWS, int CH, int NWAVES>
+struct RowStager {
+    using T = SwzTile<ROWS, CH>;
+    static constexpr int kPer = (T::kInstr + NWAVES - 1) / NWAVES;   // loads per wave, at most
+    uint32_t off[kPer];
+
+    __device__ void init(int wave, int lane, uint32_t row_stride) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int i = wave + k * NWAVES;
+            const int rs = (i < T::kInstr ? i : 0) * (64 / CH) + lane / CH;
+            off[k] = (uint32_t)rs * row_stride + (uint32_t)(((lane & (CH - 1)) ^ T::swz(rs)) << 4);
+        }
+    }
+    __device__ void issue(char *tile, int wave, int lane, const void *base, size_t row_stride,
+                          int valid_rows) const {
+        if (valid_rows < ROWS) {
+            stage_rows_async<ROWS, CH, NWAVES>(tile, wave, lane, base, row_stride, valid_rows);
+            return;
+        }
+        lds_byte *lds = (lds_byte *)tile;
+        const char *src = (const char *)base;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            if (T::kInstr % NWAVES == 0 || wave + k * NWAVES < T::kInstr)
+                __builtin_amdgcn_global_load_lds((const void *)(src + off[k]),
+                                                 lds + (wave + k * NWAVES) * 1024, 16, 0, 0);
+    }
+};
+
 // Wait for this wave's outstanding direct loads (vmcnt = 0).
 __device__ __forceinline__ void wait_async() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
