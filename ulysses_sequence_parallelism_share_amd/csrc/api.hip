@@ -60,7 +60,7 @@ size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, Attn
     w.seg_agg = (int32_t *)take(4 * segments_scratch_ints(N));
     w.qv = hkv > 1 ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
     w.dov = hkv > 1 ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
-    w.rowstat = (float2 *)take(8 * (size_t)hkv * Mpad);
+    w.rowstat = (float *)take(8 * (size_t)hkv * Mpad);
     if (ws) *ws = w;
     return off;
 }

@@ -20,9 +20,10 @@
 //  * k_attn_bwd_dq - a workgroup owns 128 virtual query rows (like the
 //    forward); Q and dO stay in registers, K and V tiles stream through LDS,
 //    and dQ^T += K^T dS^T accumulates per lane (K^T by transposing reads).
-// Both stream their tiles through double-buffered LDS filled by direct
-// global->LDS loads one tile ahead.  A pre-pass writes, per virtual row,
-// (lse * log2e, D) contiguously, so a row tile's statistics are one load.
+// Both stream their tiles through LDS rings filled by direct global->LDS
+// loads issued ahead.  A pre-pass writes the row statistics lse * log2e and
+// D per block of 32 virtual rows (32 of each, contiguous), so a row tile's
+// statistics are one load and each role reads only the half it needs.
 #include <type_traits>
 
 #include "common.h"
@@ -39,15 +40,17 @@ constexpr int BM = 128;  // virtual query rows per dQ workgroup
 constexpr int BN = 64;   // keys per dQ tile
 
 // ---------------------------------------------------------------------------
-// Row statistics: rowstat[kh][v] = (lse * log2e, rowsum(dO * O)) for every
-// virtual row v < Mpad of KV head kh; rows past M get (+inf, 0), so their
-// probabilities are exactly 0.  One group of D/8 lanes per row.
+// Row statistics of virtual row v < Mpad of KV head kh, in blocks of 32 rows:
+// with R = kh * Mpad + v, b = R / 32 and j = R % 32,
+//     rowstat[64 b + j] = lse * log2e,   rowstat[64 b + 32 + j] = rowsum(dO * O).
+// Rows past M get (+inf, 0), so their probabilities are exactly 0.  One group
+// of D/8 lanes per row.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restrict__ o,
                                                            const bf16 *__restrict__ d_o,
                                                            const float *__restrict__ lse,
-                                                           float2 *__restrict__ rowstat, int N,
+                                                           float *__restrict__ rowstat, int N,
                                                            int hq, int hkv, int g, FastDiv fg,
                                                            int Mpad) {
     constexpr int LPR = D / 8;
@@ -70,9 +73,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
     }
 #pragma unroll
     for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (in_grid && c == 0)
-        rowstat[row] = ok ? make_float2(lse[(size_t)h * N + t] * SP_LOG2E, acc)
-                          : make_float2(INFINITY, 0.f);
+    if (in_grid && c == 0) {
+        float *blk = rowstat + (row & ~(int64_t)31) * 2 + (row & 31);
+        blk[0] = ok ? lse[(size_t)h * N + t] * SP_LOG2E : INFINITY;
+        blk[32] = ok ? acc : 0.f;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -97,8 +102,10 @@ struct DkdvSmem {
     static_assert(R::kInstr <= kDkdvWaves, "at most one Q and one dO load per wave per tile");
     static_assert(BQ * 8 == kDkdvWaves * 32, "two 16-byte (lse2, D) loads per wave per tile");
     static constexpr int kQ = 0, kDO = R::kBytes, kStat = 2 * R::kBytes;
-    static constexpr int kStage = kStat + BQ * 8;   // (lse2, D) of BQ rows
-    static constexpr int kP = kDkdvStages * kStage; // P handed from A to B: [2][pair][lane][16] bf16
+    static constexpr int kStage = kStat + BQ * 8;   // lse2 of BQ rows, then D of BQ rows
+    // P handed from A to B: [2 slots][pair][2 halves][64 lanes] x 16 bytes (a
+    // 16-byte lane stride keeps the exchange bank-conflict free)
+    static constexpr int kP = kDkdvStages * kStage;
     static constexpr int kPSlot = 4 * 64 * 32;
     static constexpr int kBytes = kP + 2 * kPSlot;
 };
@@ -119,7 +126,7 @@ template <int D>
 __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ qv,
     const bf16 *__restrict__ dov, size_t v_head_stride, int v_rows,
-    const float2 *__restrict__ rowstat, const int32_t *__restrict__ kend,
+    const float *__restrict__ rowstat, const int32_t *__restrict__ kend,
     void *__restrict__ dk, void *__restrict__ dv, int N, int Mpad, int hkv, int g,
     FastDiv fg, float scale_log2, float scale, int out_f32) {
     using S = DkdvSmem<D>;
@@ -160,9 +167,9 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
         const size_t roff = (size_t)kh * v_head_stride + (size_t)vq0 * D;
         stager.issue(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
         stager.issue(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
-        if (lane < 2)   // every wave: two 16-byte pieces of the rows' (lse2, D)
+        if (lane < 2)   // every wave: two 16-byte pieces of the rows' statistics
             __builtin_amdgcn_global_load_lds(
-                (const void *)((const char *)(rowstat + (size_t)kh * Mpad + vq0) + wave * 32 + lane * 16),
+                (const void *)((const char *)(rowstat + ((size_t)kh * Mpad + vq0) * 2) + wave * 32 + lane * 16),
                 (lds_byte *)(base + S::kStat + wave * 32), 16, 0, 0);
     };
     for (int i = 0; i < kDkdvStages - 1 && i < n_it; ++i) stage(i, i);
@@ -233,8 +240,8 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
         if (t < 0 || t >= n_it) continue;
         const char *base = smem + (t % kDkdvStages) * S::kStage;
         const int vq0 = tile_row(t);
-        const f32x4 *stat = (const f32x4 *)(base + S::kStat);   // (lse2, D) of two rows
-        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot + pair * 64 * 32) + lane * 2;
+        const float *stat = (const float *)(base + S::kStat);   // lse2 of BQ rows, then D
+        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot + pair * 2048) + lane;
 
         // First product: S = Q K^T (A) or dP = dO V^T (B); lane = key.
         f32x16 x;
@@ -256,8 +263,7 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int q0 = rg * 8 + half * 4;
-                    const f32x4 st01 = stat[q0 / 2], st23 = stat[q0 / 2 + 1];
-                    const float l2[4] = {st01[0], st01[2], st23[0], st23[2]};
+                    const f32x4 l2 = *(const f32x4 *)(stat + q0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = rg * 4 + i;
@@ -275,14 +281,13 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
             else
                 softmax(std::true_type{});
             ps[0] = opnd[0];
-            ps[1] = opnd[1];
+            ps[64] = opnd[1];
         } else {
-            const bf16x8 p0 = ps[0], p1 = ps[1];
+            const bf16x8 p0 = ps[0], p1 = ps[64];
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int q0 = rg * 8 + half * 4;
-                const f32x4 st01 = stat[q0 / 2], st23 = stat[q0 / 2 + 1];
-                const float dl[4] = {st01[1], st01[3], st23[1], st23[3]};
+                const f32x4 dl = *(const f32x4 *)(stat + BQ + q0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rg * 4 + i;
@@ -336,7 +341,7 @@ struct DqSmem {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const bf16 *__restrict__ d_o, const float2 *__restrict__ rowstat,
+    const bf16 *__restrict__ d_o, const float *__restrict__ rowstat,
     const int32_t *__restrict__ kstart, void *__restrict__ dq, int N, int Mpad, int hq, int hkv,
     int g, FastDiv fg,
     float scale_log2, float scale, int n_row_tiles, int out_f32) {
@@ -373,8 +378,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
     };
     stage(jt0, 0);
 
-    const float2 st2 = rowstat[(size_t)kh * Mpad + vr];
-    const float l2 = st2.x, dl = st2.y;
+    const float *blk = rowstat + ((size_t)kh * Mpad + (vr & ~31)) * 2 + (vr & 31);
+    const float l2 = blk[0], dl = blk[32];
     bf16x8 qf[D / 16], dof[D / 16];
     {
         const size_t off = ((size_t)t * hq + h) * D + half * 8;
@@ -499,7 +504,7 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
         KernelTimer timer("attn_bwd_dkdv", stream);
         hipLaunchKernelGGL(k_attn_bwd_dkdv<D>, dim3((unsigned)(n_key_tiles * hkv)),
                            dim3(kDkdvThreads), 0, stream, (const bf16 *)k, (const bf16 *)v, qv, dov,
-                           v_head_stride, v_rows, (const float2 *)ws.rowstat,
+                           v_head_stride, v_rows, ws.rowstat,
                            (const int32_t *)ws.kend, dk, dv, (int)N, (int)Mpad, hkv, g, fg,
                            scale_log2, scale, (int)grad_f32);
     }
@@ -509,7 +514,7 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     KernelTimer timer("attn_bwd_dq", stream);
     hipLaunchKernelGGL(k_attn_bwd_dq<D>, dim3((unsigned)(n_row_tiles * hkv)), dim3(kThreads), 0,
                        stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                       (const bf16 *)d_o, (const float2 *)ws.rowstat, (const int32_t *)ws.kstart,
+                       (const bf16 *)d_o, ws.rowstat, (const int32_t *)ws.kstart,
                        dq, (int)N, (int)Mpad, hq, hkv, g, fg, scale_log2, scale, n_row_tiles,
                        (int)grad_f32);
     return hipGetLastError();

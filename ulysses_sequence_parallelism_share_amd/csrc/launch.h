@@ -39,7 +39,7 @@ struct AttnWorkspace {
     int32_t *seg_agg;  // segment pre-pass chunk aggregates
     void *qv;          // bwd, hkv > 1: Q in virtual-row order  [hkv][Mpad][d]
     void *dov;         // bwd, hkv > 1: dO in virtual-row order [hkv][Mpad][d]
-    float2 *rowstat;   // bwd: (lse*log2e, rowsum(dO*O)) per virtual row  [hkv][Mpad]
+    float *rowstat;    // bwd: lse*log2e and rowsum(dO*O) per 32-row block [hkv][Mpad/32][2][32]
 };
 
 size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws);
