@@ -83,70 +83,84 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
 // ---------------------------------------------------------------------------
 // dK, dV
 //
-// Eight waves: pair p (waves p and p+4) owns keys j0 + 32p .. +31.  Wave p
-// ("A") holds K and accumulates dV: S = Q K^T, P, then dV^T += dO^T P.
-// Wave p+4 ("B") holds V and accumulates dK: dP = dO V^T, then, with P from
-// A, dS = P * (dP - D) and dK^T += Q^T dS.  A hands P to B through LDS in
-// bf16, lane for lane in the accumulator layout both waves share (S and dP
-// are both [rows x keys] products).  Splitting the state keeps each wave
-// under 256 registers, so two waves run per SIMD and one role's softmax
-// overlaps the other's MFMAs.
+// A workgroup owns BK = 128 keys of one KV head, split over wave pairs; a
+// pair owns 32*KPW keys (KPW key blocks of 32).  Wave "A" of a pair holds K
+// and accumulates dV: S = Q K^T, P, then dV^T += dO^T P.  Wave "B" holds V
+// and accumulates dK: dP = dO V^T, then, with P from A, dS = P * (dP - D)
+// and dK^T += Q^T dS.  A hands P to B through LDS in bf16, lane for lane in
+// the accumulator layout both waves share (S and dP are both [rows x keys]
+// products).  Every Q / dO fragment read from LDS feeds KPW MFMAs (one per
+// key block), so LDS traffic per MFMA falls as 1/KPW; KPW = 1 runs 8 waves,
+// two per SIMD, KPW = 2 runs 4 waves, one per SIMD, with the accumulators in
+// the accumulation registers.
 // ---------------------------------------------------------------------------
-constexpr int kDkdvThreads = 512;
-constexpr int kDkdvWaves = kDkdvThreads / 64;
-constexpr int kDkdvStages = 4;   // LDS ring: tiles it+1 .. it+3 load while tile it is used
+constexpr int kDkdvStages = 5;   // LDS ring of query tiles
+constexpr int kDkdvAhead = 3;    // tiles staged ahead of the tile B works on
+constexpr int kDkdvKpw = 1;      // key blocks per wave (2 needs more registers than the compiler keeps in place)
 
-template <int D>
+template <int D, int KPW>
 struct DkdvSmem {
+    static constexpr int kWaves = 8 / KPW, kPairs = kWaves / 2;
     using R = SwzTile<BQ, D / 8>;    // Q or dO rows of the tile
-    static_assert(R::kInstr <= kDkdvWaves, "at most one Q and one dO load per wave per tile");
-    static_assert(BQ * 8 == kDkdvWaves * 32, "two 16-byte (lse2, D) loads per wave per tile");
+    static_assert(BQ * 8 % (kWaves * 16) == 0, "statistics split into 16-byte loads per wave");
+    static constexpr int kStatLanes = BQ * 8 / (kWaves * 16);   // 16-byte stat loads per wave
     static constexpr int kQ = 0, kDO = R::kBytes, kStat = 2 * R::kBytes;
     static constexpr int kStage = kStat + BQ * 8;   // lse2 of BQ rows, then D of BQ rows
-    // P handed from A to B: [2 slots][pair][2 halves][64 lanes] x 16 bytes (a
-    // 16-byte lane stride keeps the exchange bank-conflict free)
+    // P handed from A to B: [2 slots][pair][key block][2 halves][64 lanes] x
+    // 16 bytes (a 16-byte lane stride keeps the exchange bank-conflict free)
     static constexpr int kP = kDkdvStages * kStage;
-    static constexpr int kPSlot = 4 * 64 * 32;
+    static constexpr int kPSlot = kPairs * KPW * 2 * 64 * 16;
     static constexpr int kBytes = kP + 2 * kPSlot;
+    // direct loads per wave per tile: its share of the Q and dO rows, plus statistics
+    __device__ static constexpr int loads(int wave) {
+        int n = 0;
+        for (int i = wave; i < R::kInstr; i += kWaves) ++n;
+        return 2 * n + 1;
+    }
 };
 
-// Wait until at most `pending` tiles of this wave's direct loads are still
-// in flight; `per_tile` (1 or 3) is how many loads this wave issues per tile.
-__device__ __forceinline__ void wait_tiles(int pending, int per_tile) {
-    switch (pending * per_tile) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;      // vmcnt(0)
-        case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | 1); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0F70 | 2); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0F70 | 3); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0F70 | 6); break; // 2 tiles x 3 loads
-    }
+// Wait until at most `pending` (0..2) tiles of this wave's direct loads are
+// still in flight; PER is how many loads the wave issues per tile.
+template <int PER>
+__device__ __forceinline__ void wait_tiles(int pending) {
+    static_assert(2 * PER < 64, "vmcnt range");
+    if (pending == 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+    else if (pending == 1)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | PER);
+    else
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER));
 }
 
-template <int D>
-__global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
+template <int D, int KPW>
+__global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ qv,
     const bf16 *__restrict__ dov, size_t v_head_stride, int v_rows,
     const float *__restrict__ rowstat, const int32_t *__restrict__ kend,
     void *__restrict__ dk, void *__restrict__ dv, int N, int Mpad, int hkv, int g,
     FastDiv fg, float scale_log2, float scale, int out_f32) {
-    using S = DkdvSmem<D>;
+    using S = DkdvSmem<D, KPW>;
+    constexpr int W = S::kWaves, PAIRS = S::kPairs;
     __shared__ __attribute__((aligned(1024))) char smem[S::kBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = wave & 3;
-    const bool role_a = wave < 4;
+    const int pair = wave % PAIRS;
+    const bool role_a = wave < PAIRS;
     const int col = lane & 31, half = lane >> 5;
     const int kh = blockIdx.x % hkv;
     const int j0 = (blockIdx.x / hkv) * BK;
     const int M = N * g;
-    const int key = j0 + pair * 32 + col;
-    const bool key_ok = key < N;
-    const int my_kend = kend[key_ok ? key : N - 1];
-    const int kw0 = j0 + pair * 32;                     // the pair's first key
-    const int kw1 = min(kw0 + 31, N - 1);               // and last (if kw0 < N)
+    const int kw0 = j0 + pair * 32 * KPW;               // the pair's first key
+    const int kw1 = min(kw0 + 32 * KPW - 1, N - 1);     // and last (if kw0 < N)
     const bool pair_has_keys = kw0 < N;
     const int kend_w0 = pair_has_keys ? kend[kw0] : 0;
     const int kend_max = kend[min(j0 + BK, N) - 1];
+    int key[KPW], my_kend[KPW];
+#pragma unroll
+    for (int b = 0; b < KPW; ++b) {
+        key[b] = kw0 + 32 * b + col;
+        my_kend[b] = kend[key[b] < N ? key[b] : N - 1];
+    }
 
     // Rows [j0*g, kend_max*g) can see these keys; j0*g is a multiple of BQ.
     const int vq_lo = j0 * g;
@@ -159,7 +173,7 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
     // qv + kh*v_head_stride + v*D; `v_rows` rows exist).  Rows past the end
     // are read from the last row: finite data, and their statistics make P
     // exactly 0.
-    RowStager<BQ, D / 8, kDkdvWaves> stager;
+    RowStager<BQ, D / 8, W> stager;
     stager.init(wave, lane, D * 2);
     auto stage = [&](int it, int buf) {
         char *base = smem + buf * S::kStage;
@@ -167,33 +181,38 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
         const size_t roff = (size_t)kh * v_head_stride + (size_t)vq0 * D;
         stager.issue(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
         stager.issue(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
-        if (lane < 2)   // every wave: two 16-byte pieces of the rows' statistics
+        if (lane < S::kStatLanes)   // every wave: its 16-byte pieces of the rows' statistics
             __builtin_amdgcn_global_load_lds(
-                (const void *)((const char *)(rowstat + ((size_t)kh * Mpad + vq0) * 2) + wave * 32 + lane * 16),
-                (lds_byte *)(base + S::kStat + wave * 32), 16, 0, 0);
+                (const void *)((const char *)(rowstat + ((size_t)kh * Mpad + vq0) * 2) +
+                               (wave * S::kStatLanes + lane) * 16),
+                (lds_byte *)(base + S::kStat + wave * S::kStatLanes * 16), 16, 0, 0);
     };
-    for (int i = 0; i < kDkdvStages - 1 && i < n_it; ++i) stage(i, i);
+    for (int i = 0; i < kDkdvAhead && i < n_it; ++i) stage(i, i);
 
-    // This wave's B operand (K for A, V for B), lane = key.
-    bf16x8 kv[D / 16];
-    {
+    // This wave's B operands (K for A, V for B), lane = key.
+    bf16x8 kv[KPW][D / 16];
+#pragma unroll
+    for (int b = 0; b < KPW; ++b) {
         const bf16 *src = role_a ? k : v;
-        const size_t off = ((size_t)(key_ok ? key : 0) * hkv + kh) * D + half * 8;
+        const bool ok = key[b] < N;
+        const size_t off = ((size_t)(ok ? key[b] : 0) * hkv + kh) * D + half * 8;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
             bf16x8 a = *(const bf16x8 *)(src + off + 16 * st);
-            if (!key_ok) {
+            if (!ok) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) a[i] = (bf16)0.f;
             }
-            kv[st] = a;
+            kv[b][st] = a;
         }
     }
-    f32x16 acc[D / 32];   // dV^T (A) or dK^T (B): lane = key, registers = features
+    f32x16 acc[KPW][D / 32];   // dV^T (A) or dK^T (B): lane = key, registers = features
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i)
+    for (int b = 0; b < KPW; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+        for (int i = 0; i < D / 32; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
 
     // A runs one tile ahead of B: in iteration `it`, A turns tile it+1 into P
     // (double-buffered exchange slot) and dV, while B turns tile it and A's P
@@ -228,31 +247,49 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
         return __builtin_bit_cast(bf16x8, v);
     };
 
-    const int per_tile = wave < S::R::kInstr ? 3 : 1;   // direct loads this wave issues per tile
-    if (n_it > 0) wait_tiles(min(kDkdvStages - 2, n_it - 1), per_tile);   // tile 0
+    constexpr int PER_A = S::loads(0), PER_B = S::loads(W - 1);
+    auto wait_for = [&](int pending) {   // this wave's loads per tile decide the count
+        if (PER_A == PER_B || wave < S::R::kInstr % W || S::R::kInstr % W == 0)
+            wait_tiles<PER_A>(pending);
+        else
+            wait_tiles<PER_B>(pending);
+    };
+    if (n_it > 0) wait_for(min(kDkdvAhead - 1, n_it - 1));   // tile 0
+    int slot_a = 0, slot_st = kDkdvAhead - 1;   // ring slots of tile it+1 and of the next stage
+    auto advance = [](int x) { return x + 1 == kDkdvStages ? 0 : x + 1; };
     // Iteration -1 runs A on tile 0 only; iteration it runs A on it+1, B on it.
     for (int it = -1; it < n_it; ++it) {
-        if (it >= 0) wait_tiles(it + 2 < n_it ? 1 : 0, per_tile);   // tile it+1 for A
+        if (it >= 0) wait_for(it + 2 < n_it ? 1 : 0);   // tile it+1 for A
         __syncthreads();
-        if (it >= 0 && it + kDkdvStages - 1 < n_it)
-            stage(it + kDkdvStages - 1, (it + kDkdvStages - 1) % kDkdvStages);
+        if (it >= 0 && it + kDkdvAhead < n_it) {
+            slot_st = advance(slot_st);
+            stage(it + kDkdvAhead, slot_st);
+        }
+        const int slot_b = slot_a == 0 ? kDkdvStages - 1 : slot_a - 1;
         const int t = role_a ? it + 1 : it;
+        const int slot = role_a ? slot_a : slot_b;
+        slot_a = advance(slot_a);
         if (t < 0 || t >= n_it) continue;
-        const char *base = smem + (t % kDkdvStages) * S::kStage;
+        const char *base = smem + slot * S::kStage;
         const int vq0 = tile_row(t);
         const float *stat = (const float *)(base + S::kStat);   // lse2 of BQ rows, then D
-        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot + pair * 2048) + lane;
+        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot) + pair * KPW * 128 + lane;
 
         // First product: S = Q K^T (A) or dP = dO V^T (B); lane = key.
-        f32x16 x;
+        f32x16 x[KPW];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = 0.f;
+        for (int b = 0; b < KPW; ++b)
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st)
-            x = mfma32(*(const bf16x8 *)(base + rows1 + S::R::off(col, 2 * st + half)), kv[st], x);
+            for (int r = 0; r < 16; ++r) x[b][r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            const bf16x8 a = *(const bf16x8 *)(base + rows1 + S::R::off(col, 2 * st + half));
+#pragma unroll
+            for (int b = 0; b < KPW; ++b) x[b] = mfma32(a, kv[b][st], x[b]);
+        }
 
         // rows of accumulator register r: rg*8 + half*4 + i (r = rg*4 + i)
-        bf16x8 opnd[2];
+        bf16x8 opnd[KPW][2];
         if (role_a) {
             const int tq_first = (int)fdiv((uint32_t)vq0, fg);
             const int tq_last = (int)fdiv((uint32_t)(min(vq0 + BQ, M) - 1), fg);
@@ -267,12 +304,16 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = rg * 4 + i;
-                        float p = fast_exp2(fmaf(x[r], scale_log2, -l2[i]));
-                        if constexpr (decltype(masked)::value) {
-                            const int tq = (int)fdiv((uint32_t)(vq0 + q0 + i), fg);
-                            p = (key <= tq && tq < my_kend) ? p : 0.f;
+                        int tq = 0;
+                        if constexpr (decltype(masked)::value)
+                            tq = (int)fdiv((uint32_t)(vq0 + q0 + i), fg);
+#pragma unroll
+                        for (int b = 0; b < KPW; ++b) {
+                            float p = fast_exp2(fmaf(x[b][r], scale_log2, -l2[i]));
+                            if constexpr (decltype(masked)::value)
+                                p = (key[b] <= tq && tq < my_kend[b]) ? p : 0.f;
+                            opnd[b][r >> 3][r & 7] = (bf16)p;
                         }
-                        opnd[r >> 3][r & 7] = (bf16)p;
                     }
                 }
             };
@@ -280,10 +321,18 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
                 softmax(std::false_type{});
             else
                 softmax(std::true_type{});
-            ps[0] = opnd[0];
-            ps[64] = opnd[1];
+#pragma unroll
+            for (int b = 0; b < KPW; ++b) {
+                ps[b * 128] = opnd[b][0];
+                ps[b * 128 + 64] = opnd[b][1];
+            }
         } else {
-            const bf16x8 p0 = ps[0], p1 = ps[64];
+            bf16x8 pb[KPW][2];
+#pragma unroll
+            for (int b = 0; b < KPW; ++b) {
+                pb[b][0] = ps[b * 128];
+                pb[b][1] = ps[b * 128 + 64];
+            }
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int q0 = rg * 8 + half * 4;
@@ -291,8 +340,11 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = rg * 4 + i;
-                    const float p = (float)(r < 8 ? p0[r] : p1[r - 8]);
-                    opnd[r >> 3][r & 7] = (bf16)(p * (x[r] - dl[i]));
+#pragma unroll
+                    for (int b = 0; b < KPW; ++b) {
+                        const float p = (float)pb[b][r >> 3][r & 7];
+                        opnd[b][r >> 3][r & 7] = (bf16)(p * (x[b][r] - dl[i]));
+                    }
                 }
             }
         }
@@ -301,31 +353,37 @@ __global__ __launch_bounds__(kDkdvThreads) void k_attn_bwd_dkdv(
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                acc[db] = mfma32(tr_read(base + rows2, db, 16 * s2), opnd[s2], acc[db]);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const bf16x8 a = tr_read(base + rows2, db, 16 * s2);
+#pragma unroll
+                for (int b = 0; b < KPW; ++b) acc[b][db] = mfma32(a, opnd[b][s2], acc[b][db]);
+            }
     }
 
-    if (!key_ok) return;
     void *out = role_a ? dv : dk;
     const float mul = role_a ? 1.f : scale;
-    const size_t obase = ((size_t)key * hkv + kh) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int b = 0; b < KPW; ++b) {
+        if (key[b] >= N) continue;
+        const size_t obase = ((size_t)key[b] * hkv + kh) * D;
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const int e = db * 32 + rg * 8 + half * 4;
-            if (out_f32) {
-                f32x4 a;
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = acc[db][rg * 4 + i] * mul;
-                *(f32x4 *)((float *)out + obase + e) = a;
-            } else {
-                bf16x4 a;
+            for (int rg = 0; rg < 4; ++rg) {
+                const int e = db * 32 + rg * 8 + half * 4;
+                if (out_f32) {
+                    f32x4 a;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = (bf16)(acc[db][rg * 4 + i] * mul);
-                *(bf16x4 *)((bf16 *)out + obase + e) = a;
+                    for (int i = 0; i < 4; ++i) a[i] = acc[b][db][rg * 4 + i] * mul;
+                    *(f32x4 *)((float *)out + obase + e) = a;
+                } else {
+                    bf16x4 a;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a[i] = (bf16)(acc[b][db][rg * 4 + i] * mul);
+                    *(bf16x4 *)((bf16 *)out + obase + e) = a;
+                }
             }
-        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -502,8 +560,8 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     {
         const int n_key_tiles = (int)((N + BK - 1) / BK);
         KernelTimer timer("attn_bwd_dkdv", stream);
-        hipLaunchKernelGGL(k_attn_bwd_dkdv<D>, dim3((unsigned)(n_key_tiles * hkv)),
-                           dim3(kDkdvThreads), 0, stream, (const bf16 *)k, (const bf16 *)v, qv, dov,
+        hipLaunchKernelGGL((k_attn_bwd_dkdv<D, kDkdvKpw>), dim3((unsigned)(n_key_tiles * hkv)),
+                           dim3(64 * 8 / kDkdvKpw), 0, stream, (const bf16 *)k, (const bf16 *)v, qv, dov,
                            v_head_stride, v_rows, ws.rowstat,
                            (const int32_t *)ws.kend, dk, dv, (int)N, (int)Mpad, hkv, g, fg,
                            scale_log2, scale, (int)grad_f32);
