@@ -167,6 +167,39 @@ sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sp_attn_fwd_strided, sp_attn_bwd_strided - sp_attn_fwd and sp_attn_bwd on
+ * tensors whose tokens lie a given stride apart: element (t, h, e) of q is
+ * at q[t * q_stride + h * head_dim + e], and likewise for k and v
+ * (kv_stride, shared), o, d_o, dq, dk and dv.  Strides are in elements (of
+ * the tensor's own type), at least heads * head_dim, multiples of 8 and at
+ * most 2^24; otherwise SP_E_SHAPE.  Everything else (arguments, layouts of
+ * lse and position_ids, errors, arithmetic, determinism) is as for the
+ * unstrided calls, which are these calls with the packed strides
+ * (n_q_heads * head_dim, n_kv_heads * head_dim); results are bit-identical
+ * to theirs on the same values.
+ *
+ * Purpose: the seq->head exchange ([T] two-GPU figure; [B] "How Ulysses
+ * works", steps 1-3) gives rank r the heads [r*H/P, (r+1)*H/P) of every
+ * token.  Where the gathered tokens sit in one buffer [N][G][H][d] (the
+ * exchange buffer laid out token-major), rank r's q, k and v are that
+ * buffer at head offset r*H/P (plus g*H*d for the g-th tensor of a fused
+ * group) with stride G*H*d, so attention can read them, and write o and the
+ * gradients back, in place of separate relayout passes.
+ */
+sp_status sp_attn_fwd_strided(const void *q, int64_t q_stride, const void *k, const void *v,
+                              int64_t kv_stride, const int64_t *position_ids, int64_t n_tokens,
+                              int n_q_heads, int n_kv_heads, int head_dim, float softmax_scale,
+                              void *o, int64_t o_stride, float *lse, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+sp_status sp_attn_bwd_strided(const void *q, int64_t q_stride, const void *k, const void *v,
+                              int64_t kv_stride, const void *o, int64_t o_stride, const void *d_o,
+                              int64_t do_stride, const float *lse, const int64_t *position_ids,
+                              int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                              float softmax_scale, int grad_dtype, void *dq, int64_t dq_stride,
+                              void *dk, int64_t dk_stride, void *dv, int64_t dv_stride,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * sp_weighted_loss - token-weighted aggregation of per-rank losses ([A]
  * "ALST/Ulysses SP backend configuration", the loss loop; [B] "Loss
  * aggregation"), for all sp_size ranks at once.

@@ -124,12 +124,15 @@ def test_workspace_bytes():
     assert f(0, 4, 1, 128) == 0 or f(0, 4, 1, 128) < 4096
     small, big = f(1000, 8, 2, 128), f(2000, 8, 2, 128)
     assert 0 < small < big
-    # at least the per-token segment bounds and the per-row statistics; with
-    # several KV heads also the virtual-row copies of Q and dO
-    N, hq, d = 524288, 4, 128
-    assert f(N, hq, 1, d) >= 8 * N + 8 * hq * N
-    assert f(N, 2 * hq, 2, d) >= 8 * N + 8 * 2 * hq * N + 2 * 2 * 2 * hq * d * N
-    assert f(N, 2 * hq, 2, d) < 8 * N + 8 * 2 * hq * N + 2 * 2 * 2 * hq * d * N + (1 << 20)
+    # at least the per-token segment bounds and the per-row statistics; when
+    # the query heads per KV head do not divide 32, also the virtual-row
+    # copies of Q and dO
+    N, d = 524288, 128
+    base = lambda hq: 8 * N + 8 * hq * N
+    assert base(4) <= f(N, 4, 1, d) < base(4) + (1 << 20)
+    assert base(8) <= f(N, 8, 2, d) < base(8) + (1 << 20)          # g = 4: read in place
+    copies = 2 * 2 * 6 * d * N
+    assert base(6) + copies <= f(N, 6, 2, d) < base(6) + copies + (1 << 20)   # g = 3
 
 
 def _loss(**kw):
@@ -149,3 +152,45 @@ def test_loss_validation():
     assert _loss(**outs, tl=A16, lab=0x10004) == _lib.SP_E_ALIGN
     assert _loss(**outs, tl=0x10001, lab=A16) == _lib.SP_E_ALIGN
     assert _loss(tl=A16, lab=A16, loss=A16, rl=A16, good=0x10004) == _lib.SP_E_ALIGN
+
+
+def _fwd_s(**kw):
+    a = dict(q=None, sq=512, k=None, v=None, skv=128, pos=None, N=256, hq=4, hkv=1, d=128,
+             scale=0.0, o=None, so=512, lse=None, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.call("sp_attn_fwd_strided", a["q"], a["sq"], a["k"], a["v"], a["skv"], a["pos"],
+                     a["N"], a["hq"], a["hkv"], a["d"], a["scale"], a["o"], a["so"], a["lse"],
+                     a["ws"], a["wsb"], None)
+
+
+def _bwd_s(**kw):
+    a = dict(q=None, sq=512, k=None, v=None, skv=128, o=None, so=512, do=None, sdo=512, lse=None,
+             pos=None, N=256, hq=4, hkv=1, d=128, scale=0.0, gd=1, dq=None, sdq=512, dk=None,
+             sdk=128, dv=None, sdv=128, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.call("sp_attn_bwd_strided", a["q"], a["sq"], a["k"], a["v"], a["skv"], a["o"],
+                     a["so"], a["do"], a["sdo"], a["lse"], a["pos"], a["N"], a["hq"], a["hkv"],
+                     a["d"], a["scale"], a["gd"], a["dq"], a["sdq"], a["dk"], a["sdk"], a["dv"],
+                     a["sdv"], a["ws"], a["wsb"], None)
+
+
+def test_strided_attention_validation():
+    """Token strides must cover the heads, be multiples of 8 and at most 2^24
+    (checked before pointers, like the other shape errors)."""
+    for fn, ptrs, strides in ((_fwd_s, FWD_PTRS, ("sq", "skv", "so")),
+                              (_bwd_s, BWD_PTRS, ("sq", "skv", "so", "sdo", "sdq", "sdk", "sdv"))):
+        assert fn() == _lib.SP_E_NULL                        # packed strides, no buffers
+        assert fn(sq=4096, skv=2048, so=4096) == _lib.SP_E_NULL
+        for name in strides:
+            small = 127 if name in ("skv", "sdk", "sdv") else 511
+            assert fn(**{name: small}) == _lib.SP_E_SHAPE, name        # does not cover the heads
+            assert fn(**{name: 4100}) == _lib.SP_E_SHAPE, name         # not a multiple of 8
+            assert fn(**{name: (1 << 24) + 8}) == _lib.SP_E_SHAPE, name
+        assert fn(d=96) == _lib.SP_E_SHAPE
+        assert fn(hq=6, hkv=4) == _lib.SP_E_NOT_DIVISIBLE
+        assert fn(N=0) == _lib.SP_OK
+        p = {k: v for k, v in ptrs.items()}
+        p["q"] = MIS
+        assert fn(**p) == _lib.SP_E_ALIGN
+        assert fn(**ptrs) == _lib.SP_E_WORKSPACE
+    assert _bwd_s(gd=7) == _lib.SP_E_DTYPE

@@ -34,6 +34,11 @@ SIGNATURES = {
     "sp_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i64, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "sp_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i, _i, _i, _f, _i, _vp, _vp,
                          _vp, _vp, _sz, _vp]),
+    "sp_attn_fwd_strided": (_i, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i, _i, _i, _f, _vp, _i64,
+                                 _vp, _vp, _sz, _vp]),
+    "sp_attn_bwd_strided": (_i, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64,
+                                 _i, _i, _i, _f, _i, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz,
+                                 _vp]),
     "sp_weighted_loss": (_i, [_vp, _vp, _i, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "sp_timing_enable": (_i, [_i]),
     "sp_timing_collect": (_i, [_vp, _i]),

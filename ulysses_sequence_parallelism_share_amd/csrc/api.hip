@@ -39,6 +39,13 @@ sp_status check_attn_shape(int64_t N, int hq, int hkv, int d, float scale) {
     return SP_OK;
 }
 
+// A token stride (in elements) must cover the token's heads, keep 16-byte
+// vectors aligned and keep a tile's row offsets within 32 bits.
+constexpr int64_t kMaxStride = (int64_t)1 << 24;
+inline bool bad_stride(int64_t stride, int heads, int d) {
+    return stride < (int64_t)heads * d || stride % 8 != 0 || stride > kMaxStride;
+}
+
 inline int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -58,8 +65,9 @@ size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, Attn
     w.kstart = (int32_t *)take(4 * (size_t)N);
     w.kend = (int32_t *)take(4 * (size_t)N);
     w.seg_agg = (int32_t *)take(4 * segments_scratch_ints(N));
-    w.qv = hkv > 1 ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
-    w.dov = hkv > 1 ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
+    const bool gather = !attn_rows_direct(hq, hkv);
+    w.qv = gather ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
+    w.dov = gather ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
     w.rowstat = (float *)take(8 * (size_t)hkv * Mpad);
     if (ws) *ws = w;
     return off;
@@ -108,12 +116,17 @@ size_t sp_attn_workspace_bytes(int64_t n_tokens, int n_q_heads, int n_kv_heads, 
     return attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, nullptr, nullptr);
 }
 
-sp_status sp_attn_fwd(const void *q, const void *k, const void *v, const int64_t *position_ids,
-                      int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
-                      float softmax_scale, void *o, float *lse, void *workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+sp_status sp_attn_fwd_strided(const void *q, int64_t q_stride, const void *k, const void *v,
+                              int64_t kv_stride, const int64_t *position_ids, int64_t n_tokens,
+                              int n_q_heads, int n_kv_heads, int head_dim, float softmax_scale,
+                              void *o, int64_t o_stride, float *lse, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
     sp_status st = check_attn_shape(n_tokens, n_q_heads, n_kv_heads, head_dim, softmax_scale);
-    if (st != SP_OK || n_tokens == 0) return st;
+    if (st != SP_OK) return st;
+    if (bad_stride(q_stride, n_q_heads, head_dim) || bad_stride(kv_stride, n_kv_heads, head_dim) ||
+        bad_stride(o_stride, n_q_heads, head_dim))
+        return SP_E_SHAPE;
+    if (n_tokens == 0) return SP_OK;
     if (!q || !k || !v || !position_ids || !o || !lse) return SP_E_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
         misaligned(position_ids, 8) || misaligned(lse, 4))
@@ -124,18 +137,36 @@ sp_status sp_attn_fwd(const void *q, const void *k, const void *v, const int64_t
     AttnWorkspace ws;
     attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, workspace, &ws);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+    const AttnStrides strides{q_stride, kv_stride, o_stride, 0, 0, 0, 0};
     return launch_attn_fwd(q, k, v, position_ids, n_tokens, n_q_heads, n_kv_heads, head_dim,
-                           scale, o, lse, ws, stream) == hipSuccess ? SP_OK : SP_E_HIP;
+                           scale, o, lse, strides, ws, stream) == hipSuccess ? SP_OK : SP_E_HIP;
 }
 
-sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *d_o,
-                      const float *lse, const int64_t *position_ids, int64_t n_tokens,
-                      int n_q_heads, int n_kv_heads, int head_dim, float softmax_scale,
-                      int grad_dtype, void *dq, void *dk, void *dv, void *workspace,
+sp_status sp_attn_fwd(const void *q, const void *k, const void *v, const int64_t *position_ids,
+                      int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                      float softmax_scale, void *o, float *lse, void *workspace,
                       size_t workspace_bytes, hipStream_t stream) {
+    const int64_t sq = (int64_t)n_q_heads * head_dim, skv = (int64_t)n_kv_heads * head_dim;
+    return sp_attn_fwd_strided(q, sq, k, v, skv, position_ids, n_tokens, n_q_heads, n_kv_heads,
+                               head_dim, softmax_scale, o, sq, lse, workspace, workspace_bytes,
+                               stream);
+}
+
+sp_status sp_attn_bwd_strided(const void *q, int64_t q_stride, const void *k, const void *v,
+                              int64_t kv_stride, const void *o, int64_t o_stride, const void *d_o,
+                              int64_t do_stride, const float *lse, const int64_t *position_ids,
+                              int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                              float softmax_scale, int grad_dtype, void *dq, int64_t dq_stride,
+                              void *dk, int64_t dk_stride, void *dv, int64_t dv_stride,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
     sp_status st = check_attn_shape(n_tokens, n_q_heads, n_kv_heads, head_dim, softmax_scale);
     if (st != SP_OK) return st;
     if (grad_dtype != SP_DTYPE_BF16 && grad_dtype != SP_DTYPE_F32) return SP_E_DTYPE;
+    if (bad_stride(q_stride, n_q_heads, head_dim) || bad_stride(kv_stride, n_kv_heads, head_dim) ||
+        bad_stride(o_stride, n_q_heads, head_dim) || bad_stride(do_stride, n_q_heads, head_dim) ||
+        bad_stride(dq_stride, n_q_heads, head_dim) || bad_stride(dk_stride, n_kv_heads, head_dim) ||
+        bad_stride(dv_stride, n_kv_heads, head_dim))
+        return SP_E_SHAPE;
     if (n_tokens == 0) return SP_OK;
     if (!q || !k || !v || !o || !d_o || !lse || !position_ids || !dq || !dk || !dv) return SP_E_NULL;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
@@ -148,9 +179,21 @@ sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o
     AttnWorkspace ws;
     attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, workspace, &ws);
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+    const AttnStrides strides{q_stride, kv_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride};
     return launch_attn_bwd(q, k, v, o, d_o, lse, position_ids, n_tokens, n_q_heads, n_kv_heads,
-                           head_dim, scale, grad_dtype == SP_DTYPE_F32, dq, dk, dv, ws,
+                           head_dim, scale, grad_dtype == SP_DTYPE_F32, dq, dk, dv, strides, ws,
                            stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
+sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *d_o,
+                      const float *lse, const int64_t *position_ids, int64_t n_tokens,
+                      int n_q_heads, int n_kv_heads, int head_dim, float softmax_scale,
+                      int grad_dtype, void *dq, void *dk, void *dv, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    const int64_t sq = (int64_t)n_q_heads * head_dim, skv = (int64_t)n_kv_heads * head_dim;
+    return sp_attn_bwd_strided(q, sq, k, v, skv, o, sq, d_o, sq, lse, position_ids, n_tokens,
+                               n_q_heads, n_kv_heads, head_dim, softmax_scale, grad_dtype, dq, sq,
+                               dk, skv, dv, skv, workspace, workspace_bytes, stream);
 }
 
 sp_status sp_weighted_loss(const float *token_loss, const int64_t *shift_labels, int sp_size,

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
                                                            const float *__restrict__ lse,
                                                            float *__restrict__ rowstat, int N,
                                                            int hq, int hkv, int g, FastDiv fg,
-                                                           int Mpad) {
+                                                           int Mpad, int64_t o_st, int64_t do_st) {
     constexpr int LPR = D / 8;
     const int64_t row = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / LPR;  // kh*Mpad + v
     const int c = threadIdx.x % LPR;
@@ -65,9 +65,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
     if (ok) {
         t = (int)fdiv((uint32_t)v, fg);
         h = kh * g + (v - t * g);
-        const size_t off = ((size_t)t * hq + h) * D + c * 8;
-        const bf16x8 a = *(const bf16x8 *)(o + off);
-        const bf16x8 b = *(const bf16x8 *)(d_o + off);
+        const bf16x8 a = *(const bf16x8 *)(o + (size_t)t * o_st + h * D + c * 8);
+        const bf16x8 b = *(const bf16x8 *)(d_o + (size_t)t * do_st + h * D + c * 8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc += (float)a[i] * (float)b[i];
     }
@@ -94,6 +93,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
 // two per SIMD, KPW = 2 runs 4 waves, one per SIMD, with the accumulators in
 // the accumulation registers.
 // ---------------------------------------------------------------------------
+// Where the query rows (Q and dO) of the dK/dV kernel's KV head come from:
+// virtual row v of KV head kh at byte offset
+// kh * head_bytes + (v >> gshift) * tok_bytes + (v & (2^gshift - 1)) * d * 2;
+// `rows` rows exist.
+struct RowSource {
+    int64_t q_head_bytes, do_head_bytes;
+    uint32_t q_tok_bytes, do_tok_bytes;
+    int gshift, rows;
+};
+
 constexpr int kDkdvStages = 5;   // LDS ring of query tiles
 constexpr int kDkdvAhead = 3;    // tiles staged ahead of the tile B works on
 constexpr int kDkdvKpw = 1;      // key blocks per wave (2 needs more registers than the compiler keeps in place)
@@ -134,11 +143,11 @@ __device__ __forceinline__ void wait_tiles(int pending) {
 
 template <int D, int KPW>
 __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
-    const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ qv,
-    const bf16 *__restrict__ dov, size_t v_head_stride, int v_rows,
-    const float *__restrict__ rowstat, const int32_t *__restrict__ kend,
-    void *__restrict__ dk, void *__restrict__ dv, int N, int Mpad, int hkv, int g,
-    FastDiv fg, float scale_log2, float scale, int out_f32) {
+    const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ q_rows,
+    const bf16 *__restrict__ do_rows, RowSource rs, const float *__restrict__ rowstat,
+    const int32_t *__restrict__ kend, void *__restrict__ dk, void *__restrict__ dv, int N,
+    int Mpad, int hkv, int g, FastDiv fg, float scale_log2, float scale, int out_f32,
+    int64_t kv_st, int64_t dk_st, int64_t dv_st) {
     using S = DkdvSmem<D, KPW>;
     constexpr int W = S::kWaves, PAIRS = S::kPairs;
     __shared__ __attribute__((aligned(1024))) char smem[S::kBytes];
@@ -169,18 +178,22 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
     // tiles of one sample share that end, so workgroups running side by side
     // read the same Q and dO rows at about the same time and share them in L2.
     auto tile_row = [&](int it) { return vq_lo + (n_it - 1 - it) * BQ; };
-    // Q and dO rows come from virtual-row-major copies (row v of KV head kh at
-    // qv + kh*v_head_stride + v*D; `v_rows` rows exist).  Rows past the end
-    // are read from the last row: finite data, and their statistics make P
-    // exactly 0.
-    RowStager<BQ, D / 8, W> stager;
-    stager.init(wave, lane, D * 2);
+    // Virtual row v of KV head kh lies at byte offset kh * head_bytes +
+    // (v >> gshift) * tok_bytes + (v & (2^gshift - 1)) * D * 2 of q_rows /
+    // do_rows (`RowSource`); tiles start at multiples of 32 rows, hence at
+    // token boundaries.  Rows past the end are read from the last row: finite
+    // data, and their statistics make P exactly 0.
+    RowStager<BQ, D / 8, W> stager_q, stager_do;
+    stager_q.init(wave, lane, rs.q_tok_bytes, D * 2, rs.gshift);
+    stager_do.init(wave, lane, rs.do_tok_bytes, D * 2, rs.gshift);
+    const char *q_head = (const char *)q_rows + (size_t)kh * rs.q_head_bytes;
+    const char *do_head = (const char *)do_rows + (size_t)kh * rs.do_head_bytes;
     auto stage = [&](int it, int buf) {
         char *base = smem + buf * S::kStage;
         const int vq0 = tile_row(it);
-        const size_t roff = (size_t)kh * v_head_stride + (size_t)vq0 * D;
-        stager.issue(base + S::kQ, wave, lane, qv + roff, D * 2, v_rows - vq0);
-        stager.issue(base + S::kDO, wave, lane, dov + roff, D * 2, v_rows - vq0);
+        const size_t tok0 = (size_t)(vq0 >> rs.gshift);
+        stager_q.issue(base + S::kQ, wave, lane, q_head + tok0 * rs.q_tok_bytes, rs.rows - vq0);
+        stager_do.issue(base + S::kDO, wave, lane, do_head + tok0 * rs.do_tok_bytes, rs.rows - vq0);
         if (lane < S::kStatLanes)   // every wave: its 16-byte pieces of the rows' statistics
             __builtin_amdgcn_global_load_lds(
                 (const void *)((const char *)(rowstat + ((size_t)kh * Mpad + vq0) * 2) +
@@ -195,7 +208,7 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
     for (int b = 0; b < KPW; ++b) {
         const bf16 *src = role_a ? k : v;
         const bool ok = key[b] < N;
-        const size_t off = ((size_t)(ok ? key[b] : 0) * hkv + kh) * D + half * 8;
+        const size_t off = (size_t)(ok ? key[b] : 0) * kv_st + kh * D + half * 8;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
             bf16x8 a = *(const bf16x8 *)(src + off + 16 * st);
@@ -365,7 +378,7 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
 #pragma unroll
     for (int b = 0; b < KPW; ++b) {
         if (key[b] >= N) continue;
-        const size_t obase = ((size_t)key[b] * hkv + kh) * D;
+        const size_t obase = (size_t)key[b] * (role_a ? dv_st : dk_st) + kh * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -402,7 +415,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
     const bf16 *__restrict__ d_o, const float *__restrict__ rowstat,
     const int32_t *__restrict__ kstart, void *__restrict__ dq, int N, int Mpad, int hq, int hkv,
     int g, FastDiv fg,
-    float scale_log2, float scale, int n_row_tiles, int out_f32) {
+    float scale_log2, float scale, int n_row_tiles, int out_f32, int64_t q_st, int64_t kv_st,
+    int64_t do_st, int64_t dq_st) {
     using S = DqSmem<D>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -426,13 +440,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
     const int jt0 = key_lo / BN, jt1 = t_last / BN;
     // Keys past the end are read from the last key: finite values, always masked.
     RowStager<BN, D / 8, kWaves> stager;
-    stager.init(wave, lane, (uint32_t)(hkv * D * 2));
+    stager.init(wave, lane, (uint32_t)(kv_st * 2), 0, 0);
     auto stage = [&](int jt, int buf) {
         char *base = smem + buf * S::kStage;
         const int j0 = jt * BN;
-        const size_t roff = ((size_t)j0 * hkv + kh) * D;
-        stager.issue(base + S::kK, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
-        stager.issue(base + S::kV, wave, lane, v + roff, (size_t)hkv * D * 2, N - j0);
+        const size_t roff = (size_t)j0 * kv_st + kh * D;
+        stager.issue(base + S::kK, wave, lane, k + roff, N - j0);
+        stager.issue(base + S::kV, wave, lane, v + roff, N - j0);
     };
     stage(jt0, 0);
 
@@ -440,11 +454,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
     const float l2 = blk[0], dl = blk[32];
     bf16x8 qf[D / 16], dof[D / 16];
     {
-        const size_t off = ((size_t)t * hq + h) * D + half * 8;
+        const bf16 *qrow = q + (size_t)t * q_st + h * D + half * 8;
+        const bf16 *dorow = d_o + (size_t)t * do_st + h * D + half * 8;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            qf[s] = *(const bf16x8 *)(q + off + 16 * s);
-            dof[s] = *(const bf16x8 *)(d_o + off + 16 * s);
+            qf[s] = *(const bf16x8 *)(qrow + 16 * s);
+            dof[s] = *(const bf16x8 *)(dorow + 16 * s);
         }
     }
     f32x16 dqacc[D / 32];
@@ -505,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
     for (; jt <= jt1; ++jt) tile_step(jt, std::true_type{});
 
     if (!row_ok) return;
-    const size_t obase = ((size_t)t * hq + h) * D;
+    const size_t obase = (size_t)t * dq_st + h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -528,8 +543,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
 template <int D>
 hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o,
                       const void *d_o, const float *lse, int64_t N, int hq, int hkv, float scale,
-                      bool grad_f32, void *dq, void *dk, void *dv, const AttnWorkspace &ws,
-                      hipStream_t stream) {
+                      bool grad_f32, void *dq, void *dk, void *dv, const AttnStrides &st,
+                      const AttnWorkspace &ws, hipStream_t stream) {
     const int g = hq / hkv;
     const int64_t M = N * g;
     const int64_t Mpad = (M + 63) / 64 * 64;
@@ -542,29 +557,36 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
         KernelTimer timer("bwd_rowstats", stream);
         hipLaunchKernelGGL(k_bwd_rowstats<D>, dim3((unsigned)((threads + kThreads - 1) / kThreads)),
                            dim3(kThreads), 0, stream, (const bf16 *)o, (const bf16 *)d_o, lse,
-                           ws.rowstat, (int)N, hq, hkv, g, fg, (int)Mpad);
+                           ws.rowstat, (int)N, hq, hkv, g, fg, (int)Mpad, st.o, st.d_o);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // With one KV head the virtual rows of q and dO are their own rows; with
-    // several, row-major virtual-row copies are gathered first.
-    const bool copy_rows = hkv > 1;
-    if (copy_rows) {
-        if ((e = launch_gather_rows(q, ws.qv, N, hq, hkv, g, D, Mpad, stream)) != hipSuccess) return e;
-        if ((e = launch_gather_rows(d_o, ws.dov, N, hq, hkv, g, D, Mpad, stream)) != hipSuccess) return e;
+    // Query rows of a KV head: read in place when g divides 32, else gathered
+    // into row-major virtual-row copies first.
+    RowSource rs;
+    const bf16 *q_rows, *do_rows;
+    if (attn_rows_direct(hq, hkv)) {
+        int gshift = 0;
+        while ((1 << gshift) < g) ++gshift;
+        q_rows = (const bf16 *)q;
+        do_rows = (const bf16 *)d_o;
+        rs = {(int64_t)g * D * 2, (int64_t)g * D * 2, (uint32_t)(st.q * 2), (uint32_t)(st.d_o * 2),
+              gshift, (int)M};
+    } else {
+        if ((e = launch_gather_rows(q, st.q, ws.qv, N, hkv, g, D, Mpad, stream)) != hipSuccess) return e;
+        if ((e = launch_gather_rows(d_o, st.d_o, ws.dov, N, hkv, g, D, Mpad, stream)) != hipSuccess) return e;
+        q_rows = (const bf16 *)ws.qv;
+        do_rows = (const bf16 *)ws.dov;
+        rs = {Mpad * D * 2, Mpad * D * 2, (uint32_t)(D * 2), (uint32_t)(D * 2), 0, (int)Mpad};
     }
-    const bf16 *qv = copy_rows ? (const bf16 *)ws.qv : (const bf16 *)q;
-    const bf16 *dov = copy_rows ? (const bf16 *)ws.dov : (const bf16 *)d_o;
-    const size_t v_head_stride = copy_rows ? (size_t)Mpad * D : 0;
-    const int v_rows = copy_rows ? (int)Mpad : (int)M;
 
     {
         const int n_key_tiles = (int)((N + BK - 1) / BK);
         KernelTimer timer("attn_bwd_dkdv", stream);
         hipLaunchKernelGGL((k_attn_bwd_dkdv<D, kDkdvKpw>), dim3((unsigned)(n_key_tiles * hkv)),
-                           dim3(64 * 8 / kDkdvKpw), 0, stream, (const bf16 *)k, (const bf16 *)v, qv, dov,
-                           v_head_stride, v_rows, ws.rowstat,
+                           dim3(64 * 8 / kDkdvKpw), 0, stream, (const bf16 *)k, (const bf16 *)v,
+                           q_rows, do_rows, rs, (const float *)ws.rowstat,
                            (const int32_t *)ws.kend, dk, dv, (int)N, (int)Mpad, hkv, g, fg,
-                           scale_log2, scale, (int)grad_f32);
+                           scale_log2, scale, (int)grad_f32, st.k, st.dk, st.dv);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -572,9 +594,9 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     KernelTimer timer("attn_bwd_dq", stream);
     hipLaunchKernelGGL(k_attn_bwd_dq<D>, dim3((unsigned)(n_row_tiles * hkv)), dim3(kThreads), 0,
                        stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
-                       (const bf16 *)d_o, ws.rowstat, (const int32_t *)ws.kstart,
+                       (const bf16 *)d_o, (const float *)ws.rowstat, (const int32_t *)ws.kstart,
                        dq, (int)N, (int)Mpad, hq, hkv, g, fg, scale_log2, scale, n_row_tiles,
-                       (int)grad_f32);
+                       (int)grad_f32, st.q, st.k, st.d_o, st.dq);
     return hipGetLastError();
 }
 
@@ -583,13 +605,14 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                            const void *d_o, const float *lse, const int64_t *pos, int64_t N,
                            int hq, int hkv, int d, float scale, bool grad_f32, void *dq,
-                           void *dk, void *dv, const AttnWorkspace &ws, hipStream_t stream) {
+                           void *dk, void *dv, const AttnStrides &st, const AttnWorkspace &ws,
+                           hipStream_t stream) {
     if (N <= 0) return hipSuccess;
     hipError_t e = launch_segments(pos, ws.kstart, ws.kend, ws.seg_agg, N, stream);
     if (e != hipSuccess) return e;
     if (d == 128)
-        return bwd_launch<128>(q, k, v, o, d_o, lse, N, hq, hkv, scale, grad_f32, dq, dk, dv, ws,
-                               stream);
-    return bwd_launch<64>(q, k, v, o, d_o, lse, N, hq, hkv, scale, grad_f32, dq, dk, dv, ws,
+        return bwd_launch<128>(q, k, v, o, d_o, lse, N, hq, hkv, scale, grad_f32, dq, dk, dv, st,
+                               ws, stream);
+    return bwd_launch<64>(q, k, v, o, d_o, lse, N, hq, hkv, scale, grad_f32, dq, dk, dv, st, ws,
                           stream);
 }

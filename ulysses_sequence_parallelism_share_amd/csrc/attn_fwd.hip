@@ -55,7 +55,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const int32_t *__restrict__ kstart, bf16 *__restrict__ o, float *__restrict__ lse, int N,
-    int hq, int hkv, int g, FastDiv fg, float scale_log2, int n_row_tiles) {
+    int hq, int hkv, int g, FastDiv fg, float scale_log2, int n_row_tiles, int64_t q_st,
+    int64_t kv_st, int64_t o_st) {
     using S = FwdSmem<D>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -79,20 +80,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
     const int jt0 = key_lo / BN, jt1 = t_last / BN;
     // Keys past the end are read from the last key: finite values, always masked.
     RowStager<BN, D / 8, kWaves> stager;
-    stager.init(wave, lane, (uint32_t)(hkv * D * 2));
+    stager.init(wave, lane, (uint32_t)(kv_st * 2), 0, 0);
     auto stage = [&](int jt, int buf) {
         char *base = smem + buf * S::kStage;
         const int j0 = jt * BN;
-        const size_t roff = ((size_t)j0 * hkv + kh) * D;
-        stager.issue(base, wave, lane, k + roff, (size_t)hkv * D * 2, N - j0);
-        stager.issue(base + S::K::kBytes, wave, lane, v + roff, (size_t)hkv * D * 2, N - j0);
+        const size_t roff = (size_t)j0 * kv_st + kh * D;
+        stager.issue(base, wave, lane, k + roff, N - j0);
+        stager.issue(base + S::K::kBytes, wave, lane, v + roff, N - j0);
     };
     stage(jt0, 0);
 
     // This lane's query row as the B operand of S^T = K Q^T.
     bf16x8 qf[D / 16];
     {
-        const bf16 *qrow = q + ((size_t)t * hq + h) * D + half * 8;
+        const bf16 *qrow = q + (size_t)t * q_st + h * D + half * 8;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) qf[s] = *(const bf16x8 *)(qrow + 16 * s);
     }
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.f / l_tot;
     if (row_ok) {
-        bf16 *orow = o + ((size_t)t * hq + h) * D;
+        bf16 *orow = o + (size_t)t * o_st + h * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_fwd(
 
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const int64_t *pos,
                            int64_t N, int hq, int hkv, int d, float scale, void *o, float *lse,
-                           const AttnWorkspace &ws, hipStream_t stream) {
+                           const AttnStrides &st, const AttnWorkspace &ws, hipStream_t stream) {
     if (N <= 0) return hipSuccess;
     hipError_t e = launch_segments(pos, ws.kstart, ws.kend, ws.seg_agg, N, stream);
     if (e != hipSuccess) return e;
@@ -220,10 +221,10 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const in
     if (d == 128)
         hipLaunchKernelGGL(k_attn_fwd<128>, grid, dim3(kThreads), 0, stream, (const bf16 *)q,
                            (const bf16 *)k, (const bf16 *)v, ws.kstart, (bf16 *)o, lse,
-                           (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles);
+                           (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles, st.q, st.k, st.o);
     else
         hipLaunchKernelGGL(k_attn_fwd<64>, grid, dim3(kThreads), 0, stream, (const bf16 *)q,
                            (const bf16 *)k, (const bf16 *)v, ws.kstart, (bf16 *)o, lse,
-                           (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles);
+                           (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles, st.q, st.k, st.o);
     return hipGetLastError();
 }

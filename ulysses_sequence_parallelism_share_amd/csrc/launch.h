@@ -24,7 +24,7 @@ class KernelTimer {
 hipError_t launch_relayout(bool to_head, const void *src, void *dst, int P, int64_t N, int G,
                            int H, int d, int rank, hipStream_t stream);
 
-hipError_t launch_gather_rows(const void *src, void *dst, int64_t N, int heads_src, int n_kv,
+hipError_t launch_gather_rows(const void *src, int64_t src_stride, void *dst, int64_t N, int n_kv,
                               int g, int D, int64_t rows_pad, hipStream_t stream);
 
 // Scratch ints the segment pre-pass needs for N tokens (per-chunk aggregates).
@@ -32,26 +32,39 @@ size_t segments_scratch_ints(int64_t N);
 hipError_t launch_segments(const int64_t *pos, int32_t *kstart, int32_t *kend, int32_t *agg,
                            int64_t N, hipStream_t stream);
 
+// Token strides (in elements) of the attention tensors: element (t, h, e)
+// of q lies at q[t * q + h * d + e], and so on.  k and v share one stride.
+struct AttnStrides {
+    int64_t q, k, o, d_o, dq, dk, dv;
+};
+
 // Workspace layout shared by the forward and backward calls.
 struct AttnWorkspace {
     int32_t *kstart;   // [N]
     int32_t *kend;     // [N]
     int32_t *seg_agg;  // segment pre-pass chunk aggregates
-    void *qv;          // bwd, hkv > 1: Q in virtual-row order  [hkv][Mpad][d]
-    void *dov;         // bwd, hkv > 1: dO in virtual-row order [hkv][Mpad][d]
+    void *qv;          // bwd, groups not dividing 32: Q in virtual-row order  [hkv][Mpad][d]
+    void *dov;         // bwd, groups not dividing 32: dO in virtual-row order [hkv][Mpad][d]
     float *rowstat;    // bwd: lse*log2e and rowsum(dO*O) per 32-row block [hkv][Mpad/32][2][32]
 };
 
 size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws);
 
+// The dK/dV kernel reads query rows of one KV head straight from q and dO
+// when its g = hq/hkv query heads per token are a power of two dividing 32
+// (then every 32-row tile starts at a token boundary); otherwise they are
+// gathered into the workspace first.
+inline bool attn_rows_direct(int hq, int hkv) { return 32 % (hq / hkv) == 0; }
+
 hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const int64_t *pos,
                            int64_t N, int hq, int hkv, int d, float scale, void *o, float *lse,
-                           const AttnWorkspace &ws, hipStream_t stream);
+                           const AttnStrides &st, const AttnWorkspace &ws, hipStream_t stream);
 
 hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                            const void *d_o, const float *lse, const int64_t *pos, int64_t N,
                            int hq, int hkv, int d, float scale, bool grad_f32, void *dq,
-                           void *dk, void *dv, const AttnWorkspace &ws, hipStream_t stream);
+                           void *dk, void *dv, const AttnStrides &st, const AttnWorkspace &ws,
+                           hipStream_t stream);
 
 hipError_t launch_weighted_loss(const float *token_loss, const int64_t *labels, int P, int64_t N,
                                 int64_t ignore_index, float *loss, float *rank_loss,

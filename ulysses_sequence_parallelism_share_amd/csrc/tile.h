@@ -44,56 +44,61 @@ struct SwzTile {
     __device__ static constexpr int off(int r, int c) { return r * kStride + ((c ^ swz(r)) << 4); }
 };
 
-// Issue this wave's share of the loads of one tile whose row r is at
-// base + r * row_stride bytes.  Rows at or past `valid_rows` are read from
-// row valid_rows - 1 instead (the caller makes such rows harmless).
-template <int ROWS, int CH, int NWAVES>
-__device__ __forceinline__ void stage_rows_async(char *tile, int wave, int lane, const void *base,
-                                                 size_t row_stride, int valid_rows) {
-    using T = SwzTile<ROWS, CH>;
-    lds_byte *lds = (lds_byte *)tile;   // the tile lives in __shared__ memory
-    const char *src = (const char *)base;
-    for (int i = wave; i < T::kInstr; i += NWAVES) {
-        const int rs = i * (64 / CH) + lane / CH;          // LDS row of this slot
-        const int r = rs < valid_rows ? rs : valid_rows - 1; // global row it holds
-        const int c = (lane & (CH - 1)) ^ T::swz(rs);
-        __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)r * row_stride + c * 16),
-                                         lds + i * 1024, 16, 0, 0);
-    }
-}
-
-// The same loads with the per-lane part of each address computed once: a
-// wave keeps, for each load it issues, its lane's byte offset within the
-// source tile, so staging a full tile costs one address add per load.  Only
-// a tile with fewer than ROWS valid rows (the last one) takes the clamping
-// path above.
+// Issue this wave's share of the direct loads of one tile.  Source row r of
+// the tile (relative to the tile's base address) lies at byte offset
+//     (r >> gshift) * tok_bytes + (r & (2^gshift - 1)) * row_bytes,
+// which covers rows with one constant stride (gshift = 0, tok_bytes = the
+// stride) and the rows of several heads of one token taken together (2^gshift
+// heads per token, row_bytes apart, tokens tok_bytes apart).  The per-lane
+// part of every load's address is computed once (init); staging a full tile
+// then costs one address add per load.  In a tile with fewer than ROWS valid
+// rows (the last one), rows at or past `valid_rows` are read from row
+// valid_rows - 1 instead (the caller makes such rows harmless).
 template <int ROWS, int CH, int NWAVES>
 struct RowStager {
     using T = SwzTile<ROWS, CH>;
     static constexpr int kPer = (T::kInstr + NWAVES - 1) / NWAVES;   // loads per wave, at most
     uint32_t off[kPer];
+    uint32_t tok_bytes, row_bytes;
+    int gshift;
 
-    __device__ void init(int wave, int lane, uint32_t row_stride) {
+    __device__ uint32_t row_off(int r) const {
+        return (uint32_t)(r >> gshift) * tok_bytes + (uint32_t)(r & ((1 << gshift) - 1)) * row_bytes;
+    }
+    __device__ static bool mine(int wave, int k) {
+        return T::kInstr % NWAVES == 0 || wave + k * NWAVES < T::kInstr;
+    }
+    __device__ void init(int wave, int lane, uint32_t tok_bytes_, uint32_t row_bytes_, int gshift_) {
+        tok_bytes = tok_bytes_;
+        row_bytes = row_bytes_;
+        gshift = gshift_;
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
-            const int i = wave + k * NWAVES;
-            const int rs = (i < T::kInstr ? i : 0) * (64 / CH) + lane / CH;
-            off[k] = (uint32_t)rs * row_stride + (uint32_t)(((lane & (CH - 1)) ^ T::swz(rs)) << 4);
+            const int i = mine(wave, k) ? wave + k * NWAVES : 0;
+            const int rs = i * (64 / CH) + lane / CH;
+            off[k] = row_off(rs) + (uint32_t)(((lane & (CH - 1)) ^ T::swz(rs)) << 4);
         }
     }
-    __device__ void issue(char *tile, int wave, int lane, const void *base, size_t row_stride,
-                          int valid_rows) const {
-        if (valid_rows < ROWS) {
-            stage_rows_async<ROWS, CH, NWAVES>(tile, wave, lane, base, row_stride, valid_rows);
-            return;
-        }
+    __device__ void issue(char *tile, int wave, int lane, const void *base, int valid_rows) const {
         lds_byte *lds = (lds_byte *)tile;
         const char *src = (const char *)base;
+        if (valid_rows >= ROWS) {
 #pragma unroll
-        for (int k = 0; k < kPer; ++k)
-            if (T::kInstr % NWAVES == 0 || wave + k * NWAVES < T::kInstr)
-                __builtin_amdgcn_global_load_lds((const void *)(src + off[k]),
-                                                 lds + (wave + k * NWAVES) * 1024, 16, 0, 0);
+            for (int k = 0; k < kPer; ++k)
+                if (mine(wave, k))
+                    __builtin_amdgcn_global_load_lds((const void *)(src + off[k]),
+                                                     lds + (wave + k * NWAVES) * 1024, 16, 0, 0);
+            return;
+        }
+        for (int k = 0; k < kPer; ++k) {
+            if (!mine(wave, k)) continue;
+            const int i = wave + k * NWAVES;
+            const int rs = i * (64 / CH) + lane / CH;          // LDS row of this slot
+            const int r = rs < valid_rows ? rs : valid_rows - 1; // source row it holds
+            const int c = (lane & (CH - 1)) ^ T::swz(rs);
+            __builtin_amdgcn_global_load_lds((const void *)(src + row_off(r) + c * 16),
+                                             lds + i * 1024, 16, 0, 0);
+        }
     }
 };
 

@@ -151,6 +151,86 @@ def sp_attn_bwd(q, k, v, o, d_o, lse, position_ids, softmax_scale: float = 0.0,
     return dq, dk, dv
 
 
+def _need_rows(t: torch.Tensor, name: str, dtype, shape) -> int:
+    """A [N][h][d] view whose heads and elements are packed (strides (s, d, 1));
+    returns the token stride s."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+        raise ValueError(f"{name}: heads and elements of a token must be packed")
+    return t.stride(0)
+
+
+def sp_attn_fwd_strided(q, k, v, position_ids, softmax_scale: float = 0.0, o=None, lse=None,
+                        ws=None):
+    """sp_attn_fwd on [N][h][d] views with any token stride (e.g. one rank's
+    heads of a [N][G][H][d] exchange buffer); k and v share one stride.
+    `o` may be such a view too.  Returns (o, lse)."""
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    sq = _need_rows(q, "q", _BF16, (N, hq, d))
+    sk = _need_rows(k, "k", _BF16, (N, hkv, d))
+    if _need_rows(v, "v", _BF16, (N, hkv, d)) != sk:
+        raise ValueError("k and v must share one token stride")
+    _need(position_ids, "position_ids", torch.int64, (N,))
+    if o is None:
+        o = torch.empty((N, hq, d), dtype=_BF16, device=q.device)
+    so = _need_rows(o, "o", _BF16, (N, hq, d))
+    if lse is None:
+        lse = torch.empty((hq, N), dtype=torch.float32, device=q.device)
+    _need(lse, "lse", torch.float32, (hq, N))
+    if ws is None:
+        ws = workspace(N, hq, hkv, d, q.device)
+    _lib.check("sp_attn_fwd_strided", _lib.call(
+        "sp_attn_fwd_strided", _ptr(q), sq, _ptr(k), _ptr(v), sk, _ptr(position_ids), N, hq, hkv,
+        d, float(softmax_scale), _ptr(o), so, _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return o, lse
+
+
+def sp_attn_bwd_strided(q, k, v, o, d_o, lse, position_ids, softmax_scale: float = 0.0,
+                        grad_dtype=torch.float32, dq=None, dk=None, dv=None, ws=None):
+    """sp_attn_bwd on [N][h][d] views with any token stride (see
+    sp_attn_fwd_strided); dq, dk, dv may be such views too."""
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    sq = _need_rows(q, "q", _BF16, (N, hq, d))
+    sk = _need_rows(k, "k", _BF16, (N, hkv, d))
+    if _need_rows(v, "v", _BF16, (N, hkv, d)) != sk:
+        raise ValueError("k and v must share one token stride")
+    so = _need_rows(o, "o", _BF16, (N, hq, d))
+    sdo = _need_rows(d_o, "d_o", _BF16, (N, hq, d))
+    _need(lse, "lse", torch.float32, (hq, N))
+    _need(position_ids, "position_ids", torch.int64, (N,))
+    if grad_dtype == torch.float32:
+        code = _lib.SP_DTYPE_F32
+    elif grad_dtype == torch.bfloat16:
+        code = _lib.SP_DTYPE_BF16
+    else:
+        raise TypeError("grad_dtype must be torch.float32 or torch.bfloat16")
+    if dq is None:
+        dq = torch.empty((N, hq, d), dtype=grad_dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((N, hkv, d), dtype=grad_dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((N, hkv, d), dtype=grad_dtype, device=q.device)
+    sdq = _need_rows(dq, "dq", grad_dtype, (N, hq, d))
+    sdk = _need_rows(dk, "dk", grad_dtype, (N, hkv, d))
+    sdv = _need_rows(dv, "dv", grad_dtype, (N, hkv, d))
+    if ws is None:
+        ws = workspace(N, hq, hkv, d, q.device)
+    _lib.check("sp_attn_bwd_strided", _lib.call(
+        "sp_attn_bwd_strided", _ptr(q), sq, _ptr(k), _ptr(v), sk, _ptr(o), so, _ptr(d_o), sdo,
+        _ptr(lse), _ptr(position_ids), N, hq, hkv, d, float(softmax_scale), code, _ptr(dq), sdq,
+        _ptr(dk), sdk, _ptr(dv), sdv, _ptr(ws), ws.numel(), _stream()))
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------------------
 # Loss
 # ---------------------------------------------------------------------------
