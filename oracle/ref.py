@@ -11,6 +11,9 @@ out in float64 with no blocking beyond what is stated:
   for head sharding (Transformers guide "Ulysses sequence parallelism",
   introduction and its two-GPU figure; blog "Ulysses Sequence Parallelism:
   Training with Million-Token Contexts", "How Ulysses works", steps 1, 3, 5).
+  For fewer KV heads than ranks (on which the pages are silent) the exchange
+  copies each KV head to the ranks whose query heads use it, and the
+  gradient exchange sums the copies (its adjoint).
 * mask - causal attention within each packed sample, with sample boundaries
   read from position_ids rather than a 4D mask (Transformers guide,
   "Configuration", the sp_attn_implementation item; Accelerate guide
@@ -93,6 +96,69 @@ def head_to_seq(x_head: np.ndarray, sp_size: int, rank: int = -1,
     v = x_head.reshape(G, P, T, hl, d)            # [g][p][t][hl][e]
     out[:, :, :, rank * hl:(rank + 1) * hl, :] = v.transpose(1, 2, 0, 3, 4)
     return out
+
+
+def kv_head_start(n_kv: int, sp_size: int, rank: int) -> int:
+    """First KV head rank ``rank`` holds.  With n_kv >= sp_size it holds the
+    block [r*n_kv/P, (r+1)*n_kv/P); with fewer KV heads than ranks (P a
+    multiple of n_kv) it holds the single KV head its query heads use: query
+    heads [r*Hq/P, (r+1)*Hq/P) all map to KV head r // (P/n_kv) when query
+    head h uses KV head h // (Hq/n_kv).  Both are (r*n_kv) // P."""
+    return (rank * n_kv) // sp_size
+
+
+def seq_to_head_kv(x_seq: np.ndarray, rank: int = -1) -> np.ndarray:
+    """The seq->head exchange of K/V-like tensors, also for fewer KV heads than
+    ranks (then each KV head is sent to the P/n_kv ranks that use it):
+        out[q][g][p*N/P + t][i][e] = x_seq[p][t][g][kv_head_start(q) + i][e]
+    for i < hl = max(n_kv/P, 1).  x_seq is [P][N/P][G][n_kv][d]; rank == -1
+    returns [P][G][N][hl][d], rank == r rank r's [G][N][hl][d].  Bits are
+    moved verbatim."""
+    P, T, G, H, d = x_seq.shape
+    if (H >= P and H % P) or (H < P and P % H):
+        raise ValueError("KV heads and sp_size must divide one another")
+    hl = max(H // P, 1)
+    out = np.empty((P, G, P * T, hl, d), dtype=x_seq.dtype)
+    for q in range(P):
+        h0 = kv_head_start(H, P, q)
+        part = x_seq[:, :, :, h0:h0 + hl, :]                     # [p][t][g][i][e]
+        out[q] = part.transpose(2, 0, 1, 3, 4).reshape(G, P * T, hl, d)
+    return out if rank < 0 else np.ascontiguousarray(out[rank])
+
+
+def _bf16_bits_round(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest, ties to even (finite input)."""
+    b = x32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def head_to_seq_kv_sum(x_head: np.ndarray, n_kv: int, rank: int = -1,
+                       bf16_bits: bool = False) -> np.ndarray:
+    """The head->seq exchange of K/V gradients: the adjoint of seq_to_head_kv.
+    Every rank that received a copy of KV head j contributes its gradient, and
+    the copies are summed:
+        out[p][t][g][j][e] = sum over ranks q holding head j, ascending q, of
+                             x_head[q][g][p*N/P + t][j - kv_head_start(q)][e].
+    x_head is [P][G][N][hl][d].  The sum runs in float32 for float32 and bf16
+    input (bf16_bits=True: uint16 bit patterns, widened exactly, the float32
+    sum rounded once to bf16, nearest-even) and in float64 for float64 input.
+    rank == r returns only rank r's tokens, [N/P][G][n_kv][d]."""
+    P, G, N, hl, d = x_head.shape
+    T = N // P
+    if bf16_bits:
+        xs = (x_head.astype(np.uint32) << 16).view(np.float32)
+        acc_t = np.float32
+    else:
+        xs = x_head
+        acc_t = np.float64 if x_head.dtype == np.float64 else np.float32
+    acc = np.zeros((P, T, G, n_kv, d), dtype=acc_t)
+    for q in range(P):                                          # ascending rank order
+        h0 = kv_head_start(n_kv, P, q)
+        part = xs[q].reshape(G, P, T, hl, d).transpose(1, 2, 0, 3, 4).astype(acc_t)
+        acc[:, :, :, h0:h0 + hl, :] += part
+    out = _bf16_bits_round(acc) if bf16_bits else acc.astype(x_head.dtype)
+    return out if rank < 0 else np.ascontiguousarray(out[rank])
 
 
 def gather_share(x_seq: np.ndarray, rank: int, g0: int = 0, g1: int | None = None) -> np.ndarray:

@@ -130,6 +130,116 @@ def test_head_divisibility_golden():
 
 
 # ---------------------------------------------------------------------------
+# K/V relayout with fewer KV heads than ranks (replicate forward, sum backward)
+# ---------------------------------------------------------------------------
+
+KV_SHAPES = [  # P, T, G, n_kv, d
+    (4, 3, 2, 2, 8),     # 2 ranks per KV head
+    (8, 2, 1, 1, 4),     # every rank holds the single KV head
+    (4, 3, 2, 8, 4),     # more KV heads than ranks: the plain exchange
+    (6, 2, 2, 3, 8),     # 2 ranks per KV head, odd counts
+]
+
+
+@pytest.mark.parametrize("P,T,G,H,d", KV_SHAPES)
+def test_kv_relayout_brute_force(P, T, G, H, d):
+    """Loops over every output element; rank q's first KV head is q*H//P, which is
+    the KV head of its query heads under the consecutive GQA grouping."""
+    x = _rand(11, (P, T, G, H, d))
+    y = ref.seq_to_head_kv(x)
+    hl = max(H // P, 1)
+    Hq = 2 * max(H, P)                       # any query-head count divisible by both
+    for q in range(P):
+        q_heads = range(q * Hq // P, (q + 1) * Hq // P)
+        kv_of_q = {h // (Hq // H) for h in q_heads}
+        assert min(kv_of_q) == q * H // P and len(kv_of_q) == hl
+        for g in range(G):
+            for n in range(P * T):
+                for i in range(hl):
+                    assert np.array_equal(y[q, g, n, i], x[n // T, n % T, g, q * H // P + i])
+    z = ref.head_to_seq_kv_sum(y.astype(np.float64), H)
+    for p in range(P):
+        for t in range(T):
+            for g in range(G):
+                for j in range(H):
+                    want = sum(y[q, g, p * T + t, j - q * H // P] for q in range(P)
+                               if q * H // P <= j < q * H // P + hl)
+                    assert np.allclose(z[p, t, g, j], want, rtol=0, atol=1e-15)
+    assert np.array_equal(ref.seq_to_head_kv(x, rank=1), y[1])
+    assert np.array_equal(ref.head_to_seq_kv_sum(y, H, rank=P - 1), ref.head_to_seq_kv_sum(y, H)[P - 1])
+
+
+def test_kv_relayout_is_plain_exchange_when_heads_cover_ranks():
+    x = gen.normal_bf16((3, 1), (4, 5, 2, 8, 16))
+    y = ref.seq_to_head_kv(x)
+    assert np.array_equal(y, ref.seq_to_head(x))
+    assert np.array_equal(ref.head_to_seq_kv_sum(y, 8, bf16_bits=True), x)   # one copy each
+
+
+def test_kv_replication_equals_repeated_heads():
+    """Sending KV head j to P/n_kv ranks is the plain exchange of the tensor whose
+    heads are repeated P/n_kv times."""
+    P, H = 8, 2
+    x = gen.normal_bf16((3, 2), (P, 4, 2, H, 16))
+    assert np.array_equal(ref.seq_to_head_kv(x), ref.seq_to_head(np.repeat(x, P // H, axis=3)))
+
+
+def test_kv_gradient_sum_is_the_adjoint():
+    """<s2h(x), y> == <x, h2s_sum(y)>: the summed gradient exchange is the adjoint of
+    the replicating exchange (exact here: small integers in float64)."""
+    rng = np.random.default_rng(5)
+    for P, T, G, H, d in KV_SHAPES:
+        x = rng.integers(-8, 9, (P, T, G, H, d)).astype(np.float64)
+        y = rng.integers(-8, 9, (P, G, P * T, max(H // P, 1), d)).astype(np.float64)
+        assert np.sum(ref.seq_to_head_kv(x) * y) == np.sum(x * ref.head_to_seq_kv_sum(y, H))
+
+
+def test_kv_gradient_sum_bf16_rounding():
+    """bf16 copies are summed in float32 in ascending rank order and rounded once,
+    to nearest even: 1 + 2^-8 is a tie and rounds to 1; 1 + 2^-8 + 2^-8 = 1 + 2^-7
+    is exact; -(1 + 3*2^-9) rounds to -(1 + 2^-7)."""
+    def bits(v):
+        return (np.array(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    for vals, want in (([1.0, 2.0 ** -8], 1.0), ([1.0, 2.0 ** -8, 2.0 ** -8], 1.0 + 2.0 ** -7),
+                       ([-1.0, -3 * 2.0 ** -9], -(1.0 + 2.0 ** -7))):
+        P = len(vals)
+        y = np.stack([np.full((1, P, 1, 8), bits(v), np.uint16) for v in vals])   # [P][G][N][1][d]
+        z = ref.head_to_seq_kv_sum(y, 1, bf16_bits=True)
+        assert np.all(z == bits(want)), (vals, want)
+
+
+def test_gqa_layer_with_kv_replication_matches_unsharded():
+    """8 query heads, 2 KV heads, sp_size 4: each rank gets 2 query heads through the
+    plain exchange and its one KV head through the replicating exchange; its attention
+    equals the unsharded GQA attention on its heads, and the summed dK/dV equal the
+    unsharded ones."""
+    P, N, Hq, H, d = 4, 48, 8, 2, 8
+    T = N // P
+    pos = gen.position_ids_from_lengths([20, 1, 27])
+    q_seq = _rand(21, (P, T, 1, Hq, d))
+    kv_seq = _rand(22, (P, T, 2, H, d))
+    do_seq = _rand(23, (P, T, 1, Hq, d))
+    qh = ref.seq_to_head(q_seq)
+    kvh = ref.seq_to_head_kv(kv_seq)                      # [P][2][N][1][d]
+    doh = ref.seq_to_head(do_seq)
+    q_full, do_full = q_seq.reshape(N, Hq, d), do_seq.reshape(N, Hq, d)
+    k_full, v_full = kv_seq.reshape(N, 2, H, d)[:, 0], kv_seq.reshape(N, 2, H, d)[:, 1]
+    o_ref, _ = ref.attn_fwd(q_full, k_full, v_full, pos)
+    dq_ref, dk_ref, dv_ref = ref.attn_bwd(q_full, k_full, v_full, do_full, pos)
+    dkv_h = np.empty((P, 2, N, 1, d))
+    hl = Hq // P
+    for r in range(P):
+        o, _ = ref.attn_fwd(qh[r, 0], kvh[r, 0], kvh[r, 1], pos)
+        assert np.allclose(o, o_ref[:, r * hl:(r + 1) * hl], rtol=0, atol=1e-12)
+        dq, dk, dv = ref.attn_bwd(qh[r, 0], kvh[r, 0], kvh[r, 1], doh[r, 0], pos)
+        assert np.allclose(dq, dq_ref[:, r * hl:(r + 1) * hl], rtol=0, atol=1e-12)
+        dkv_h[r, 0], dkv_h[r, 1] = dk, dv
+    dkv_seq = ref.head_to_seq_kv_sum(dkv_h, H).reshape(N, 2, H, d)
+    assert np.allclose(dkv_seq[:, 0], dk_ref, rtol=0, atol=1e-12)
+    assert np.allclose(dkv_seq[:, 1], dv_ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # Mask
 # ---------------------------------------------------------------------------
 
