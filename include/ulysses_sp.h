@@ -104,6 +104,50 @@ sp_status ulysses_head_to_seq(const void *x_head, void *x_seq, int sp_size, int6
                               hipStream_t stream);
 
 /*
+ * ulysses_seq_to_head_kv - the seq->head exchange of a K/V-like tensor with
+ * n_kv_heads KV heads, also when there are fewer KV heads than ranks.
+ *
+ * The pages ask for head counts divisible by sp_size ([T] "Configuration")
+ * and do not treat grouped-query models with fewer KV heads than ranks.
+ * Query head h uses KV head h / (Hq / n_kv_heads), so rank q's query heads
+ * all use KV head (q * n_kv_heads) / sp_size; with n_kv_heads < sp_size
+ * (sp_size a multiple of n_kv_heads) each KV head is copied to the
+ * sp_size / n_kv_heads ranks that use it.  With n_kv_heads >= sp_size
+ * (n_kv_heads a multiple of sp_size) this is ulysses_seq_to_head.
+ *
+ *   x_seq   [sp_size][n_tokens/sp_size][n_groups][n_kv_heads][head_dim]  (read)
+ *   x_head  rank == -1: [sp_size][n_groups][n_tokens][hl][head_dim]
+ *           rank ==  r: [n_groups][n_tokens][hl][head_dim]   (written)
+ *   with hl = max(n_kv_heads / sp_size, 1); rank q holds KV heads
+ *   [(q*n_kv_heads)/sp_size, ... + hl).  Elements are 16-bit and moved
+ *   verbatim.  head_dim must be a multiple of 8 (SP_E_SHAPE); n_kv_heads and
+ *   sp_size must divide one another and n_tokens % sp_size == 0
+ *   (SP_E_NOT_DIVISIBLE); pointers 16-byte aligned.
+ */
+sp_status ulysses_seq_to_head_kv(const void *x_seq, void *x_head, int sp_size, int64_t n_tokens,
+                                 int n_groups, int n_kv_heads, int head_dim, int rank,
+                                 hipStream_t stream);
+
+/*
+ * ulysses_head_to_seq_kv_grad - the head->seq exchange of K/V gradients:
+ * the adjoint of ulysses_seq_to_head_kv.  Every rank that received a copy
+ * of a KV head contributes its gradient and the copies are summed:
+ *   x_seq[p][t][g][j][e] = sum over ranks q holding head j (ascending q) of
+ *                          x_head[q][g][p*N/P + t][j - (q*n_kv)/P][e]
+ * in fp32, rounded once to the element type.
+ *
+ *   x_head  [sp_size][n_groups][n_tokens][hl][head_dim]  (read; all ranks)
+ *   x_seq   rank == -1: [sp_size][n_tokens/sp_size][n_groups][n_kv_heads][head_dim]
+ *           rank ==  r: rank r's tokens only, [n_tokens/sp_size][n_groups][n_kv_heads][head_dim]
+ *   dtype   SP_DTYPE_BF16 or SP_DTYPE_F32: element type of both buffers
+ *           (else SP_E_DTYPE)
+ * Other errors as for ulysses_seq_to_head_kv.  Deterministic.
+ */
+sp_status ulysses_head_to_seq_kv_grad(const void *x_head, void *x_seq, int sp_size,
+                                      int64_t n_tokens, int n_groups, int n_kv_heads,
+                                      int head_dim, int dtype, int rank, hipStream_t stream);
+
+/*
  * sp_attn_workspace_bytes - size of the device workspace sp_attn_fwd and
  * sp_attn_bwd need for these sizes (the same buffer serves both calls; its
  * contents need no initialisation and are not preserved).  Returns 0 for

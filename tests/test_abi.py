@@ -194,3 +194,38 @@ def test_strided_attention_validation():
         assert fn(**p) == _lib.SP_E_ALIGN
         assert fn(**ptrs) == _lib.SP_E_WORKSPACE
     assert _bwd_s(gd=7) == _lib.SP_E_DTYPE
+
+
+def _kv_s2h(**kw):
+    a = dict(src=None, dst=None, P=4, N=1024, G=2, H=2, d=64, rank=-1)
+    a.update(kw)
+    return _lib.call("ulysses_seq_to_head_kv", a["src"], a["dst"], a["P"], a["N"], a["G"], a["H"],
+                     a["d"], a["rank"], None)
+
+
+def _kv_h2s(**kw):
+    a = dict(src=None, dst=None, P=4, N=1024, G=2, H=2, d=64, dt=0, rank=-1)
+    a.update(kw)
+    return _lib.call("ulysses_head_to_seq_kv_grad", a["src"], a["dst"], a["P"], a["N"], a["G"],
+                     a["H"], a["d"], a["dt"], a["rank"], None)
+
+
+@pytest.mark.parametrize("fn", [_kv_s2h, _kv_h2s])
+def test_kv_relayout_validation(fn):
+    assert fn() == _lib.SP_E_NULL                        # 2 KV heads over 4 ranks: valid
+    assert fn(H=8) == _lib.SP_E_NULL                     # more KV heads than ranks: valid
+    assert fn(H=1, P=8) == _lib.SP_E_NULL
+    assert fn(H=3) == _lib.SP_E_NOT_DIVISIBLE            # 3 and 4 do not divide one another
+    assert fn(H=6) == _lib.SP_E_NOT_DIVISIBLE
+    assert fn(N=1022) == _lib.SP_E_NOT_DIVISIBLE
+    assert fn(d=4) == _lib.SP_E_SHAPE                    # rows are moved in 16-byte chunks
+    assert fn(P=0) == _lib.SP_E_SHAPE
+    assert fn(rank=4) == _lib.SP_E_RANK
+    assert fn(N=0) == _lib.SP_OK
+    assert fn(src=MIS, dst=A16) == _lib.SP_E_ALIGN
+    assert fn(src=A16, dst=None) == _lib.SP_E_NULL
+
+
+def test_kv_grad_dtype():
+    assert _kv_h2s(dt=1) == _lib.SP_E_NULL               # fp32 is valid
+    assert _kv_h2s(dt=5) == _lib.SP_E_DTYPE

@@ -30,6 +30,8 @@ SIGNATURES = {
     "sp_abi_version": (_i, []),
     "ulysses_seq_to_head": (_i, [_vp, _vp, _i, _i64, _i, _i, _i, _i, _vp]),
     "ulysses_head_to_seq": (_i, [_vp, _vp, _i, _i64, _i, _i, _i, _i, _vp]),
+    "ulysses_seq_to_head_kv": (_i, [_vp, _vp, _i, _i64, _i, _i, _i, _i, _vp]),
+    "ulysses_head_to_seq_kv_grad": (_i, [_vp, _vp, _i, _i64, _i, _i, _i, _i, _i, _vp]),
     "sp_attn_workspace_bytes": (_sz, [_i64, _i, _i, _i]),
     "sp_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i64, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "sp_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i, _i, _i, _f, _i, _vp, _vp,

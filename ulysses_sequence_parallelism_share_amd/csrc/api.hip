@@ -30,6 +30,24 @@ sp_status check_relayout(const void *src, const void *dst, int P, int64_t N, int
     return SP_OK;
 }
 
+// K/V exchange: n_kv and sp_size must divide one another; 16-byte chunks.
+sp_status check_kv_relayout(const void *src, const void *dst, int P, int64_t N, int G, int H,
+                            int d, int rank) {
+    if (P < 1 || N < 0 || G < 1 || H < 1 || d < 1) return SP_E_SHAPE;
+    if (N % P != 0) return SP_E_NOT_DIVISIBLE;
+    if ((H >= P && H % P != 0) || (H < P && P % H != 0)) return SP_E_NOT_DIVISIBLE;
+    if (rank < -1 || rank >= P) return SP_E_RANK;
+    if (d % 8 != 0) return SP_E_SHAPE;
+    const int64_t hl = H >= P ? H / P : 1;
+    if (N * hl * (d / 8) >= ((int64_t)1 << 31) || (N / P) * G * H * (d / 8) >= ((int64_t)1 << 31) ||
+        (int64_t)P * G > 65535)
+        return SP_E_SHAPE;
+    if (N == 0) return SP_OK;
+    if (src == nullptr || dst == nullptr) return SP_E_NULL;
+    if (misaligned(src, 16) || misaligned(dst, 16)) return SP_E_ALIGN;
+    return SP_OK;
+}
+
 sp_status check_attn_shape(int64_t N, int hq, int hkv, int d, float scale) {
     if (N < 0 || hq < 1 || hkv < 1) return SP_E_SHAPE;
     if (d != 64 && d != 128) return SP_E_SHAPE;
@@ -109,6 +127,28 @@ sp_status ulysses_head_to_seq(const void *x_head, void *x_seq, int sp_size, int6
     if (st != SP_OK || n_tokens == 0) return st;
     return launch_relayout(false, x_head, x_seq, sp_size, n_tokens, n_groups, n_heads, head_dim,
                            rank, stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
+sp_status ulysses_seq_to_head_kv(const void *x_seq, void *x_head, int sp_size, int64_t n_tokens,
+                                 int n_groups, int n_kv_heads, int head_dim, int rank,
+                                 hipStream_t stream) {
+    sp_status st = check_kv_relayout(x_seq, x_head, sp_size, n_tokens, n_groups, n_kv_heads,
+                                     head_dim, rank);
+    if (st != SP_OK || n_tokens == 0) return st;
+    return launch_kv_seq_to_head(x_seq, x_head, sp_size, n_tokens, n_groups, n_kv_heads, head_dim,
+                                 rank, stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
+sp_status ulysses_head_to_seq_kv_grad(const void *x_head, void *x_seq, int sp_size,
+                                      int64_t n_tokens, int n_groups, int n_kv_heads,
+                                      int head_dim, int dtype, int rank, hipStream_t stream) {
+    if (dtype != SP_DTYPE_BF16 && dtype != SP_DTYPE_F32) return SP_E_DTYPE;
+    sp_status st = check_kv_relayout(x_head, x_seq, sp_size, n_tokens, n_groups, n_kv_heads,
+                                     head_dim, rank);
+    if (st != SP_OK || n_tokens == 0) return st;
+    return launch_kv_head_to_seq_sum(x_head, x_seq, sp_size, n_tokens, n_groups, n_kv_heads,
+                                     head_dim, dtype == SP_DTYPE_F32, rank, stream) == hipSuccess
+               ? SP_OK : SP_E_HIP;
 }
 
 size_t sp_attn_workspace_bytes(int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim) {

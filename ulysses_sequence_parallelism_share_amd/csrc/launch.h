@@ -24,6 +24,11 @@ class KernelTimer {
 hipError_t launch_relayout(bool to_head, const void *src, void *dst, int P, int64_t N, int G,
                            int H, int d, int rank, hipStream_t stream);
 
+hipError_t launch_kv_seq_to_head(const void *x_seq, void *x_head, int P, int64_t N, int G, int H,
+                                 int d, int rank, hipStream_t stream);
+hipError_t launch_kv_head_to_seq_sum(const void *x_head, void *x_seq, int P, int64_t N, int G,
+                                     int H, int d, bool f32, int rank, hipStream_t stream);
+
 hipError_t launch_gather_rows(const void *src, int64_t src_stride, void *dst, int64_t N, int n_kv,
                               int g, int D, int64_t rows_pad, hipStream_t stream);
 

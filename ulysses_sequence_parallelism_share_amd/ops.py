@@ -81,6 +81,49 @@ def ulysses_head_to_seq(x_head: torch.Tensor, sp_size: int, rank: int = -1,
     return out
 
 
+def ulysses_seq_to_head_kv(x_seq: torch.Tensor, rank: int = -1, out: torch.Tensor | None = None):
+    """K/V exchange, also for fewer KV heads than ranks: [P][N/P][G][n_kv][d] ->
+    [P][G][N][hl][d] (rank -1) or [G][N][hl][d] (rank r), hl = max(n_kv/P, 1)."""
+    if x_seq.dim() != 5:
+        raise ValueError("x_seq must be [P][N/P][G][n_kv][d]")
+    P, T, G, H, d = x_seq.shape
+    _need(x_seq, "x_seq", _BF16)
+    hl = max(H // P, 1)
+    shape = (P, G, P * T, hl, d) if rank < 0 else (G, P * T, hl, d)
+    if out is None:
+        out = torch.empty(shape, dtype=_BF16, device=x_seq.device)
+    _need(out, "out", _BF16, shape)
+    _lib.check("ulysses_seq_to_head_kv", _lib.call(
+        "ulysses_seq_to_head_kv", _ptr(x_seq), _ptr(out), P, P * T, G, H, d, rank, _stream()))
+    return out
+
+
+def ulysses_head_to_seq_kv_grad(x_head: torch.Tensor, n_kv_heads: int, rank: int = -1,
+                                out: torch.Tensor | None = None):
+    """Adjoint of ulysses_seq_to_head_kv (copies of a KV head summed in fp32):
+    [P][G][N][hl][d] -> [P][N/P][G][n_kv][d] (rank -1) or rank r's [N/P][G][n_kv][d].
+    bf16 or fp32."""
+    if x_head.dim() != 5:
+        raise ValueError("x_head must be [P][G][N][hl][d]")
+    P, G, N, hl, d = x_head.shape
+    dt = x_head.dtype
+    if dt == torch.float32:
+        code = _lib.SP_DTYPE_F32
+    elif dt == _BF16:
+        code = _lib.SP_DTYPE_BF16
+    else:
+        raise TypeError("x_head must be bfloat16 or float32")
+    _need(x_head, "x_head", dt)
+    shape = (P, N // P, G, n_kv_heads, d) if rank < 0 else (N // P, G, n_kv_heads, d)
+    if out is None:
+        out = torch.empty(shape, dtype=dt, device=x_head.device)
+    _need(out, "out", dt, shape)
+    _lib.check("ulysses_head_to_seq_kv_grad", _lib.call(
+        "ulysses_head_to_seq_kv_grad", _ptr(x_head), _ptr(out), P, N, G, n_kv_heads, d, code, rank,
+        _stream()))
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
