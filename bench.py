@@ -163,7 +163,8 @@ def summarize_traffic(fetch_csv, write_csv):
         out.append(f"# {counter}: copy reads {cal:.1f} KiB -> factor {factors[counter]:.4f} "
                    "(bytes per counted byte)")
         for kernel, sym in KERNEL_SYMBOL.items():
-            pat = re.compile(r"(^|[\s:])" + sym + r"[<(]")
+            # demangled "...::k_name<...>(" or, where the profiler leaves it mangled, "<len>k_nameI"
+            pat = re.compile(r"(^|[\s:\d])" + sym + r"([<(]|I[LZN])")
             vals = [v for n, v in rows if pat.search(n)]
             if vals:
                 per_kernel.setdefault(kernel, {})[counter] = (sum(vals) / len(vals), len(vals))
@@ -384,6 +385,39 @@ def main():
         "frac_mfma_attention_kernels": (fwd_flop + bwd_flop) / attn_kernel_ms / 1e9 / PEAK_BF16_TFLOPS,
         "frac_mfma_step": value / PEAK_BF16_TFLOPS,
     }
+    zero_copy = None
+    if relayout_in_step:
+        # The same step with attention reading rank 0's heads in place from the
+        # exchange buffers and writing O and the gradients back (no relayouts).
+        Hq, Hkv = q_seq.shape[3], kv_seq.shape[3]
+        Qv = q_seq.view(N, 1, Hq, d)[:, 0, :hq]
+        KVv = kv_seq.view(N, 2, Hkv, d)
+        DOv = do_seq.view(N, 1, Hq, d)[:, 0, :hq]
+        Ov = o_seq.view(N, 1, Hq, d)[:, 0, :hq]
+        DQv = dq_seq.view(N, 1, Hq, d)[:, 0, :hq]
+        DKVv = dkv_seq.view(N, 2, Hkv, d)
+
+        def zc_step():
+            o_, lse_ = ops.sp_attn_fwd_strided(Qv, KVv[:, 0, :hkv], KVv[:, 1, :hkv], pos, o=Ov,
+                                               lse=lse, ws=ws)
+            ops.sp_attn_bwd_strided(Qv, KVv[:, 0, :hkv], KVv[:, 1, :hkv], Ov, DOv, lse, pos,
+                                    grad_dtype=torch.bfloat16, dq=DQv, dk=DKVv[:, 0, :hkv],
+                                    dv=DKVv[:, 1, :hkv], ws=ws)
+            ops.sp_weighted_loss(token_loss, labels, out=loss_out)
+
+        zc_step()
+        torch.cuda.synchronize()
+        z0, z1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        z0.record()
+        for _ in range(args.steps):
+            zc_step()
+        z1.record()
+        torch.cuda.synchronize()
+        zc_ms = z0.elapsed_time(z1) / args.steps
+        zero_copy = {"ms_per_step": zc_ms, "TFLOP/s": (fwd_flop + bwd_flop) / zc_ms / 1e9,
+                     "note": "attention on strided views of the exchange buffers, no relayouts"}
+        log(f"[bench] zero-copy step: {zc_ms:.3f} ms/step")
+
     relayout = None
     if relayout_in_step:
         rl_ms = per_step.get("relayout_seq_to_head", 0.0) + per_step.get("relayout_head_to_seq", 0.0)
@@ -418,6 +452,7 @@ def main():
         "cpu_baseline": cpu,
         "attention": attention,
         "relayout_step": relayout,
+        "zero_copy_step": zero_copy,
         "relayout_bound": relayout_bound_out,
         "kernels_ms_per_step": per_step,
     }
