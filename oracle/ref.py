@@ -384,3 +384,39 @@ def weighted_loss(token_loss, shift_labels, ignore_index=IGNORE_INDEX):
     loss = total / max(T, 1)
     dtl = np.where(valid, 1.0 / max(T, 1), 0.0)
     return float(loss), rank_loss, good, dtl
+
+
+# ---------------------------------------------------------------------------
+# Per-token cross-entropy from hidden states (the loss the model computes
+# from shift_labels before the aggregation above; the Accelerate guide,
+# "ALST/Ulysses SP backend configuration", and the blog, "Loss aggregation",
+# recommend computing it with a fused logit-loss that never holds the full
+# logits tensor).  Written here as its plain definition.
+# ---------------------------------------------------------------------------
+
+def linear_cross_entropy(x, w, labels, g=None, ignore_index=IGNORE_INDEX):
+    """Token losses of logits = x w^T against labels, and their gradients.
+
+    x [N][K] hidden states, w [V][K] LM-head matrix (float64 or bf16 bit
+    patterns as uint16), labels [N] int64 (ignore_index: no loss), g [N]
+    upstream gradient of the token losses (None: forward only).
+        lse_t  = log sum_v exp(logit_tv)
+        loss_t = lse_t - logit_{t, labels_t}       (0 where ignored)
+        G_tv   = g_t (softmax_v(logit_t) - [v == labels_t])   (0 rows where ignored)
+        dx = G w,   dw = G^T x
+    Returns token_loss [N], lse [N] and, with g, dx [N][K], dw [V][K] (float64)."""
+    x, w = _as_f64(x), _as_f64(w)
+    labels = np.asarray(labels)
+    logits = x @ w.T
+    m = logits.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(logits - m).sum(axis=1, keepdims=True)))[:, 0]
+    valid = labels != ignore_index
+    idx = np.where(valid, labels, 0).astype(np.int64)
+    target = logits[np.arange(len(labels)), idx]
+    token_loss = np.where(valid, lse - target, 0.0)
+    if g is None:
+        return token_loss, lse
+    G = np.exp(logits - lse[:, None])
+    G[np.arange(len(labels)), idx] -= 1.0
+    G *= (np.asarray(g, dtype=np.float64) * valid)[:, None]
+    return token_loss, lse, G @ w, G.T @ x

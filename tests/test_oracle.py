@@ -574,3 +574,83 @@ def test_generator_is_deterministic_and_chunked():
     assert np.array_equal(a, b)
     tail = gen.f32_to_bf16_bits(np.random.default_rng([1, 1, 1]).standard_normal(5, dtype=np.float32))
     assert np.array_equal(a[gen.CHUNK:], tail)
+
+
+# ---------------------------------------------------------------------------
+# Per-token cross-entropy from hidden states (fused-logit-loss definition)
+# ---------------------------------------------------------------------------
+
+def _lce_case(seed, N=6, K=5, V=9, ignore=(1,)):
+    r = np.random.default_rng(seed)
+    x, w = r.standard_normal((N, K)), r.standard_normal((V, K))
+    lab = r.integers(0, V, N)
+    for i in ignore:
+        lab[i] = -100
+    return x, w, lab, r.standard_normal(N)
+
+
+def test_lce_matches_library_log_softmax():
+    from scipy.special import log_softmax, logsumexp
+    x, w, lab, _ = _lce_case(1)
+    tl, lse = ref.linear_cross_entropy(x, w, lab)
+    logits = x @ w.T
+    assert np.allclose(lse, logsumexp(logits, axis=1), rtol=0, atol=1e-12)
+    ls = log_softmax(logits, axis=1)
+    for t, y in enumerate(lab):
+        assert tl[t] == 0.0 if y == -100 else abs(tl[t] + ls[t, y]) < 1e-12
+
+
+def test_lce_gradients_finite_differences():
+    x, w, lab, g = _lce_case(2)
+    _, _, dx, dw = ref.linear_cross_entropy(x, w, lab, g)
+    f = lambda xx, ww: float(np.dot(g, ref.linear_cross_entropy(xx, ww, lab)[0]))
+    h = 1e-6
+    for arr, grad, which in ((x, dx, 0), (w, dw, 1)):
+        num = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[i] += h
+            m[i] -= h
+            num[i] = (f(p, w) - f(m, w)) / (2 * h) if which == 0 else (f(x, p) - f(x, m)) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-7), which
+
+
+def test_lce_closed_forms():
+    """w = 0: every logit is 0, loss = ln V, dx = 0, dw_v = sum_t g_t (1/V - [y_t = v]) x_t.
+    One vocabulary entry: loss 0 and zero gradients."""
+    x, _, lab, g = _lce_case(3, V=7)
+    V = 7
+    tl, lse, dx, dw = ref.linear_cross_entropy(x, np.zeros((V, x.shape[1])), lab, g)
+    valid = lab != -100
+    assert np.allclose(tl, np.where(valid, math.log(V), 0.0), rtol=0, atol=1e-14)
+    assert np.allclose(lse, math.log(V), rtol=0, atol=1e-14)
+    assert np.all(dx == 0)
+    want = np.zeros_like(dw)
+    for t in range(len(lab)):
+        if valid[t]:
+            want += g[t] * (1.0 / V) * x[t]
+            want[lab[t]] -= g[t] * x[t]
+    assert np.allclose(dw, want, rtol=0, atol=1e-13)
+    x1, w1, lab1, g1 = _lce_case(4, V=1, ignore=())
+    lab1[:] = 0
+    tl1, _, dx1, dw1 = ref.linear_cross_entropy(x1, w1, lab1, g1)
+    assert np.allclose(tl1, 0, atol=1e-14) and np.allclose(dx1, 0, atol=1e-14) and np.allclose(dw1, 0, atol=1e-14)
+
+
+def test_lce_shift_invariance_and_ignored_tokens():
+    """Adding one vector to every row of w shifts all logits of a token equally: the
+    losses and dx do not change.  Ignored tokens have no loss and no gradient; all
+    ignored gives zeros."""
+    x, w, lab, g = _lce_case(5)
+    tl, lse, dx, dw = ref.linear_cross_entropy(x, w, lab, g)
+    c = np.random.default_rng(6).standard_normal(w.shape[1])
+    tl2, _, dx2, _ = ref.linear_cross_entropy(x, w + c, lab, g)
+    assert np.allclose(tl, tl2, rtol=0, atol=1e-12) and np.allclose(dx, dx2, rtol=0, atol=1e-12)
+    assert tl[1] == 0 and np.all(dx[1] == 0)
+    x0 = x.copy()
+    x0[1] += 100.0                                     # an ignored token's values do not matter
+    _, _, dx0, dw0 = ref.linear_cross_entropy(x0, w, lab, g)
+    assert np.allclose(dw0, dw, rtol=0, atol=1e-12)
+    lab_all = np.full_like(lab, -100)
+    tla, _, dxa, dwa = ref.linear_cross_entropy(x, w, lab_all, g)
+    assert np.all(tla == 0) and np.all(dxa == 0) and np.all(dwa == 0)
