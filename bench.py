@@ -45,6 +45,8 @@ def parse():
                     help="timed round trips of the relayout-bound workload (0: skip)")
     ap.add_argument("--cpu-tokens", type=int, default=20480,
                     help="tokens of the oracle's CPU-baseline sample (0: skip)")
+    ap.add_argument("--lce-steps", type=int, default=3,
+                    help="timed calls of the fused cross-entropy workload (0: skip)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="print a text summary of a rocprofv3 --stats kernel table and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -256,6 +258,48 @@ def relayout_bound(dev, reps):
     return out
 
 
+def linear_ce_bench(dev, steps):
+    """The fused per-token cross-entropy on the Llama-3-8B-shaped LM head: 4096 tokens
+    (one chunk), hidden 4096, vocabulary 128256, forward and both gradients per call;
+    algorithmic FLOP 6*N*V*K (three products)."""
+    import torch
+    from synth import configs
+    from ulysses_sequence_parallelism_share_amd import ops
+    w = configs.LCE_WORKLOADS[13]
+    inp = configs.lce_inputs(w)
+    x, mat = to_dev_bf16(inp["x"], dev), to_dev_bf16(inp["w"], dev)
+    lab = torch.from_numpy(inp["labels"]).to(dev)
+    g = torch.from_numpy(inp["g"]).to(dev)
+    N, K, V = w.n_tokens, w.hidden, w.vocab
+    out = ops.sp_linear_ce(x, mat, lab, g, chunk_tokens=N)
+    nb = int(ops._lib.call("sp_linear_ce_workspace_bytes", V, N))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    ops.sp_linear_ce(x, mat, lab, g, chunk_tokens=N, out=out, ws=ws)
+    torch.cuda.synchronize()
+    ops.sp_timing_enable(True)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        ops.sp_linear_ce(x, mat, lab, g, chunk_tokens=N, out=out, ws=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    kt = ops.sp_timing_collect()
+    ops.sp_timing_enable(False)
+    ms = t0.elapsed_time(t1) / steps
+    gemm_flop = 2.0 * N * V * K
+    kernels = {k: v["avg_ms"] for k, v in kt.items()}
+    dom = max(("lce_gemm_logits", "lce_gemm_dx", "lce_gemm_dw"), key=lambda n: kernels[n])
+    tf = gemm_flop / kernels[dom] / 1e9
+    res = {"workload": w.name, "ms_per_call": ms, "TFLOP/s": 3 * gemm_flop / ms / 1e9,
+           "frac_mfma": 3 * gemm_flop / ms / 1e9 / PEAK_BF16_TFLOPS, "kernels_ms": kernels,
+           "roofline": {"kernel": dom, "bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                        "algorithmic_flop_per_launch": gemm_flop}}
+    del x, mat, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -433,6 +477,13 @@ def main():
         relayout_bound_out = relayout_bound(dev, args.relayout_reps)
         log(f"[bench] relayout-bound workload done in {time.time() - t1:.1f}s")
 
+    lce = None
+    if args.lce_steps > 0:
+        t1 = time.time()
+        lce = linear_ce_bench(dev, args.lce_steps)
+        log(f"[bench] linear cross-entropy: {lce['ms_per_call']:.2f} ms/call "
+            f"({time.time() - t1:.1f}s)")
+
     cpu = None
     if args.cpu_tokens > 0:
         t1 = time.time()
@@ -453,6 +504,7 @@ def main():
         "attention": attention,
         "relayout_step": relayout,
         "zero_copy_step": zero_copy,
+        "linear_ce": lce,
         "relayout_bound": relayout_bound_out,
         "kernels_ms_per_step": per_step,
     }

@@ -244,6 +244,48 @@ sp_status sp_attn_bwd_strided(const void *q, int64_t q_stride, const void *k, co
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sp_linear_ce_workspace_bytes - workspace sp_linear_ce needs for this
+ * vocabulary size and token chunk (0 for invalid sizes).
+ */
+size_t sp_linear_ce_workspace_bytes(int64_t vocab, int64_t chunk_tokens);
+
+/*
+ * sp_linear_ce - per-token cross-entropy of the logits x w^T against labels,
+ * and its gradients, without holding the logits of more than one chunk of
+ * tokens: the fused logit-loss the pages recommend for long sequences ([A]
+ * "ALST/Ulysses SP backend configuration", the note after the loss loop;
+ * [B] "Loss aggregation").  Its token losses feed sp_weighted_loss.
+ *
+ *   x            [n_tokens][hidden] bf16 (read): hidden states of this
+ *                rank's tokens
+ *   w            [vocab][hidden] bf16 (read): LM-head matrix
+ *   labels       [n_tokens] int64 (read): target ids (shift_labels);
+ *                ignore_index marks tokens without a loss; any other value
+ *                outside [0, vocab) gives a NaN loss and no gradient
+ *   d_token_loss [n_tokens] fp32 (read) or NULL: upstream gradient g of the
+ *                token losses.  For the token-weighted loss it is
+ *                sp_weighted_loss's d_token_loss (1/T on valid tokens), which
+ *                depends only on the labels.  NULL: forward only.
+ *   token_loss   [n_tokens] fp32 (written): lse_t - x_t.w_{y_t} (0 if ignored)
+ *   lse          [n_tokens] fp32 (written): log sum_v exp(x_t.w_v)
+ *   dx           [n_tokens][hidden] (written if d_token_loss): G w, with
+ *                G_tv = g_t (softmax_v - [v == y_t]); fp32 or bf16 by grad_dtype
+ *   dw           [vocab][hidden] fp32 (written if d_token_loss): G^T x
+ *   chunk_tokens tokens per chunk: a positive multiple of 64; the workspace
+ *                holds that many rows of fp32 logits and bf16 G
+ *   workspace    >= sp_linear_ce_workspace_bytes(vocab, chunk_tokens) bytes,
+ *                256-byte aligned
+ * hidden must be a positive multiple of 128 (<= 65536), else SP_E_SHAPE.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; fp32 log-sum-exp;
+ * G rounded to bf16 for the two gradient products.  Deterministic.
+ */
+sp_status sp_linear_ce(const void *x, const void *w, const int64_t *labels, int64_t ignore_index,
+                       const float *d_token_loss, int64_t n_tokens, int64_t vocab, int64_t hidden,
+                       int grad_dtype, float *token_loss, float *lse, void *dx, float *dw,
+                       int64_t chunk_tokens, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
  * sp_weighted_loss - token-weighted aggregation of per-rank losses ([A]
  * "ALST/Ulysses SP backend configuration", the loss loop; [B] "Loss
  * aggregation"), for all sp_size ranks at once.

@@ -119,3 +119,41 @@ def loss_inputs(w: Workload) -> dict:
     n_prompt = int(round(w.prompt_frac * N))
     labels[:n_prompt] = IGNORE_INDEX
     return {"token_loss": token_loss, "shift_labels": labels.reshape(P, N // P)}
+
+
+# ---------------------------------------------------------------------------
+# Per-token cross-entropy from hidden states (the loss ahead of the
+# token-weighted aggregation): hidden states x ~ N(0,1), an LM-head matrix
+# w ~ N(0, 1/hidden) (logits of order 1), labels uniform over the vocabulary
+# with the first `prompt_frac` of the tokens ignored (a prompt prefix).
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class LceWorkload:
+    cfg: int
+    name: str
+    n_tokens: int
+    hidden: int
+    vocab: int
+    prompt_frac: float = 0.1
+
+
+LCE_WORKLOADS = {
+    11: LceWorkload(11, "lce-small-n300-v1000-k256", 300, 256, 1000),
+    12: LceWorkload(12, "lce-llama2-vocab-n1024-v32000-k1024", 1024, 1024, 32000),
+    13: LceWorkload(13, "lce-llama3-8b-lmhead-n4096-v128256-k4096", 4096, 4096, 128256),
+}
+
+
+def lce_inputs(w: LceWorkload) -> dict:
+    """x [N][K] and w [V][K] bf16 bit patterns, labels [N] int64 (IGNORE_INDEX for
+    the prompt prefix) and the token-weighted loss's upstream gradient g [N]
+    (1/T on valid tokens)."""
+    x = gen.normal_bf16((w.cfg, 1), (w.n_tokens, w.hidden))
+    mat = gen.normal_bf16_scaled((w.cfg, 2), (w.vocab, w.hidden), 1.0 / w.hidden ** 0.5)
+    labels = gen.integers_i64((w.cfg, 6), (w.n_tokens,), 0, w.vocab)
+    n_prompt = int(round(w.prompt_frac * w.n_tokens))
+    labels[:n_prompt] = IGNORE_INDEX
+    T = int((labels != IGNORE_INDEX).sum())
+    g = np.where(labels != IGNORE_INDEX, 1.0 / max(T, 1), 0.0).astype(np.float32)
+    return {"x": x, "w": mat, "labels": labels, "g": g}

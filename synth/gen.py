@@ -69,6 +69,20 @@ def normal_bf16(key, shape) -> np.ndarray:
     return _chunked(tuple(key), n, fill, out).reshape(shape)
 
 
+def normal_bf16_scaled(key, shape, scale: float) -> np.ndarray:
+    """bf16 ~ N(0, scale^2) bit patterns: float32 standard normal times scale,
+    rounded to nearest-even bf16."""
+    shape = tuple(int(s) for s in shape)
+    n = int(np.prod(shape)) if shape else 1
+    out = np.empty(n, dtype=np.uint16)
+    sc = np.float32(scale)
+
+    def fill(rng, lo, hi):
+        out[lo:hi] = f32_to_bf16_bits(rng.standard_normal(hi - lo, dtype=np.float32) * sc)
+
+    return _chunked(tuple(key), n, fill, out).reshape(shape)
+
+
 def raw_bits_u16(key, shape) -> np.ndarray:
     """Uniformly random 16-bit patterns: every bf16 class appears (NaN payloads, +-0, subnormals, +-Inf)."""
     shape = tuple(int(s) for s in shape)

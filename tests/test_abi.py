@@ -229,3 +229,34 @@ def test_kv_relayout_validation(fn):
 def test_kv_grad_dtype():
     assert _kv_h2s(dt=1) == _lib.SP_E_NULL               # fp32 is valid
     assert _kv_h2s(dt=5) == _lib.SP_E_DTYPE
+
+
+def _lce(**kw):
+    a = dict(x=None, w=None, lab=None, ign=-100, g=None, N=300, V=1000, K=256, gd=1, tl=None,
+             lse=None, dx=None, dw=None, chunk=128, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.call("sp_linear_ce", a["x"], a["w"], a["lab"], a["ign"], a["g"], a["N"], a["V"],
+                     a["K"], a["gd"], a["tl"], a["lse"], a["dx"], a["dw"], a["chunk"], a["ws"],
+                     a["wsb"], None)
+
+
+def test_linear_ce_validation():
+    ptrs = dict(x=A16, w=A16, lab=A16, tl=A16, lse=A16)
+    assert _lce() == _lib.SP_E_NULL
+    assert _lce(K=200) == _lib.SP_E_SHAPE                 # hidden: multiple of 128
+    assert _lce(K=0) == _lib.SP_E_SHAPE
+    assert _lce(V=0) == _lib.SP_E_SHAPE
+    assert _lce(chunk=100) == _lib.SP_E_SHAPE             # chunk: multiple of 64
+    assert _lce(chunk=0) == _lib.SP_E_SHAPE
+    assert _lce(gd=3) == _lib.SP_E_DTYPE
+    assert _lce(N=0) == _lib.SP_OK
+    assert _lce(**ptrs, g=A16) == _lib.SP_E_NULL          # gradients requested, no dx/dw
+    assert _lce(**ptrs) == _lib.SP_E_WORKSPACE
+    need = _lib.call("sp_linear_ce_workspace_bytes", 1000, 128)
+    assert need >= 128 * 1024 * 6
+    assert _lce(**ptrs, ws=A16, wsb=need - 1) == _lib.SP_E_WORKSPACE
+    assert _lce(**ptrs, ws=A16 + 16, wsb=need) == _lib.SP_E_ALIGN    # workspace: 256-byte aligned
+    p = dict(ptrs)
+    p["x"] = MIS
+    assert _lce(**p, ws=A16, wsb=need) == _lib.SP_E_ALIGN
+    assert _lib.call("sp_linear_ce_workspace_bytes", 1000, 100) == 0

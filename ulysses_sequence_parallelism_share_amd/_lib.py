@@ -41,6 +41,9 @@ SIGNATURES = {
     "sp_attn_bwd_strided": (_i, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64,
                                  _i, _i, _i, _f, _i, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _sz,
                                  _vp]),
+    "sp_linear_ce_workspace_bytes": (_sz, [_i64, _i64]),
+    "sp_linear_ce": (_i, [_vp, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i, _vp, _vp, _vp, _vp,
+                          _i64, _vp, _sz, _vp]),
     "sp_weighted_loss": (_i, [_vp, _vp, _i, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "sp_timing_enable": (_i, [_i]),
     "sp_timing_collect": (_i, [_vp, _i]),

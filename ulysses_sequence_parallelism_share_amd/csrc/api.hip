@@ -236,6 +236,42 @@ sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o
                                dk, skv, dv, skv, workspace, workspace_bytes, stream);
 }
 
+size_t sp_linear_ce_workspace_bytes(int64_t vocab, int64_t chunk_tokens) {
+    if (vocab < 1 || vocab >= ((int64_t)1 << 30) || chunk_tokens < 64 || chunk_tokens % 64 != 0 ||
+        chunk_tokens >= ((int64_t)1 << 24))
+        return 0;
+    return lce_workspace_layout(vocab, chunk_tokens, nullptr, nullptr);
+}
+
+sp_status sp_linear_ce(const void *x, const void *w, const int64_t *labels, int64_t ignore_index,
+                       const float *d_token_loss, int64_t n_tokens, int64_t vocab, int64_t hidden,
+                       int grad_dtype, float *token_loss, float *lse, void *dx, float *dw,
+                       int64_t chunk_tokens, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    if (n_tokens < 0 || vocab < 1 || vocab >= ((int64_t)1 << 30) || hidden < 128 ||
+        hidden % 128 != 0 || hidden > 65536 || n_tokens >= ((int64_t)1 << 31))
+        return SP_E_SHAPE;
+    if (chunk_tokens < 64 || chunk_tokens % 64 != 0 || chunk_tokens >= ((int64_t)1 << 24))
+        return SP_E_SHAPE;
+    if ((size_t)vocab * hidden >= ((size_t)1 << 40)) return SP_E_SHAPE;
+    if (grad_dtype != SP_DTYPE_BF16 && grad_dtype != SP_DTYPE_F32) return SP_E_DTYPE;
+    if (n_tokens == 0) return SP_OK;
+    if (!x || !w || !labels || !token_loss || !lse) return SP_E_NULL;
+    if (d_token_loss && (!dx || !dw)) return SP_E_NULL;
+    if (misaligned(x, 16) || misaligned(w, 16) || misaligned(labels, 8) ||
+        misaligned(token_loss, 4) || misaligned(lse, 4) || misaligned(d_token_loss, 4) ||
+        misaligned(dx, 16) || misaligned(dw, 16))
+        return SP_E_ALIGN;
+    const size_t need = lce_workspace_layout(vocab, chunk_tokens, nullptr, nullptr);
+    if (!workspace || workspace_bytes < need) return SP_E_WORKSPACE;
+    if (misaligned(workspace, 256)) return SP_E_ALIGN;
+    LceWorkspace ws;
+    lce_workspace_layout(vocab, chunk_tokens, workspace, &ws);
+    return launch_linear_ce(x, w, labels, ignore_index, d_token_loss, n_tokens, vocab, hidden,
+                            grad_dtype == SP_DTYPE_F32, token_loss, lse, dx, dw, chunk_tokens, ws,
+                            stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
 sp_status sp_weighted_loss(const float *token_loss, const int64_t *shift_labels, int sp_size,
                            int64_t n_tokens, int64_t ignore_index, float *loss, float *rank_loss,
                            int64_t *good_tokens, float *d_token_loss, hipStream_t stream) {

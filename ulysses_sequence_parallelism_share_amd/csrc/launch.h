@@ -71,6 +71,22 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const vo
                            void *dk, void *dv, const AttnStrides &st, const AttnWorkspace &ws,
                            hipStream_t stream);
 
+// Workspace of the fused linear cross-entropy: one chunk of fp32 logits and
+// of the bf16 softmax gradient, both [rows][v_pad] with v_pad = vocab rounded
+// up to 128.
+struct LceWorkspace {
+    float *logits;
+    void *g;
+    int64_t v_pad;
+};
+
+size_t lce_workspace_layout(int64_t vocab, int64_t chunk, void *base, LceWorkspace *ws);
+
+hipError_t launch_linear_ce(const void *x, const void *w, const int64_t *labels,
+                            int64_t ignore_index, const float *g, int64_t N, int64_t V, int64_t K,
+                            bool dx_f32, float *token_loss, float *lse, void *dx, float *dw,
+                            int64_t chunk, const LceWorkspace &ws, hipStream_t stream);
+
 hipError_t launch_weighted_loss(const float *token_loss, const int64_t *labels, int P, int64_t N,
                                 int64_t ignore_index, float *loss, float *rank_loss,
                                 int64_t *good, float *d_token_loss, hipStream_t stream);

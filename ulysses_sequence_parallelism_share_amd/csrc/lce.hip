@@ -1,0 +1,150 @@
+// Per-token cross-entropy from hidden states and an LM-head matrix, with
+// its gradients, never holding more than one chunk of logits.
+//
+// The model computes a per-token loss from shift_labels before the
+// token-weighted aggregation (Accelerate guide "Sequence parallelism in
+// accelerate", "ALST/Ulysses SP backend configuration", the loss loop and
+// the note after it; blog "Ulysses Sequence Parallelism: Training with
+// Million-Token Contexts", "Loss aggregation"); for long sequences the
+// pages recommend a fused logit-loss that never materialises the full
+// logits tensor.  For tokens t, vocabulary entries v:
+//     lse_t  = log sum_v exp(x_t . w_v),  loss_t = lse_t - x_t . w_{y_t}
+//     G_tv   = g_t (softmax_v - [v == y_t]),  dX = G W,  dW = G^T X
+// (ignored tokens: no loss, no gradient).  Tokens are processed in chunks:
+// logits of the chunk (one GEMM), a row pass (log-sum-exp, loss and G in
+// bf16), then dX of the chunk and dW += G^T X (two GEMMs).  Only the
+// chunk's logits (fp32) and G (bf16) live in the workspace.
+#include "common.h"
+#include "launch.h"
+
+hipError_t launch_gemm_logits(const void *x, int x_rows, const void *w, int w_rows, int64_t K,
+                              float *logits, int64_t ldl, int64_t M, int64_t N,
+                              hipStream_t stream);
+hipError_t launch_gemm_dx(const void *g, int64_t ldg, int g_rows, const void *w, int w_rows,
+                          int64_t Kv, void *dx, bool dx_f32, int64_t N, int m_store, int64_t M,
+                          hipStream_t stream);
+hipError_t launch_gemm_dw(const void *g, int64_t ldg, const void *x, int x_rows, int64_t Kt,
+                          float *dw, int64_t N, int m_store, int64_t M, hipStream_t stream);
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float x, float *red, bool is_max) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float y = __shfl_xor(x, o);
+        x = is_max ? fmaxf(x, y) : x + y;
+    }
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = x;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+    return r;
+}
+
+// One workgroup per token row of the chunk (rows at or past n_tok only
+// clear their G row, so the dW product's padded k-range adds nothing).
+// Labels outside [0, V) other than ignore_index give a NaN loss and no
+// gradient.
+__global__ __launch_bounds__(kThreads) void k_lce_rows(
+    const float *__restrict__ logits, int64_t ldl, int V, int v_pad,
+    const int64_t *__restrict__ labels, int64_t ignore_index, const float *__restrict__ g,
+    int n_tok, float *__restrict__ token_loss, float *__restrict__ lse_out,
+    bf16 *__restrict__ G, int64_t ldg) {
+    __shared__ float red[kThreads / 64];
+    const int row = blockIdx.x;
+    if (row >= n_tok) {
+        if (G)
+            for (int v = threadIdx.x; v < v_pad; v += kThreads) G[(size_t)row * ldg + v] = (bf16)0.f;
+        return;
+    }
+    const float *l = logits + (size_t)row * ldl;
+    float mx = -INFINITY;
+    for (int v = threadIdx.x; v < V; v += kThreads) mx = fmaxf(mx, l[v]);
+    mx = block_reduce(mx, red, true);
+    float s = 0.f;
+    for (int v = threadIdx.x; v < V; v += kThreads) s += fast_exp2((l[v] - mx) * SP_LOG2E);
+    s = block_reduce(s, red, false);
+    const float lse = mx + __logf(s);
+    const int64_t y = labels[row];
+    const bool ignored = y == ignore_index;
+    const bool in_range = y >= 0 && y < V;
+    const bool valid = !ignored && in_range;
+    if (threadIdx.x == 0) {
+        lse_out[row] = lse;
+        token_loss[row] = valid ? lse - l[y] : (ignored ? 0.f : NAN);
+    }
+    if (!G) return;
+    const float gt = valid ? g[row] : 0.f;
+    const float sh = lse * SP_LOG2E;
+    bf16 *gr = G + (size_t)row * ldg;
+    for (int v = threadIdx.x; v < v_pad; v += kThreads) {
+        float x = 0.f;
+        if (v < V) x = gt * (fast_exp2(fmaf(l[v], SP_LOG2E, -sh)) - (v == y ? 1.f : 0.f));
+        gr[v] = (bf16)x;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_fill_zero(f32x4 *__restrict__ p, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < n4) p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+size_t lce_workspace_layout(int64_t vocab, int64_t chunk, void *base, LceWorkspace *ws) {
+    const int64_t v_pad = round_up(vocab, 128);
+    const size_t logits_bytes = (size_t)chunk * v_pad * 4;
+    const size_t g_bytes = (size_t)round_up(chunk, 64) * v_pad * 2;
+    const size_t a = (logits_bytes + 255) & ~(size_t)255;
+    if (ws) {
+        ws->logits = base ? (float *)base : nullptr;
+        ws->g = base ? (char *)base + a : nullptr;
+        ws->v_pad = v_pad;
+    }
+    return a + ((g_bytes + 255) & ~(size_t)255);
+}
+
+hipError_t launch_linear_ce(const void *x, const void *w, const int64_t *labels,
+                            int64_t ignore_index, const float *g, int64_t N, int64_t V, int64_t K,
+                            bool dx_f32, float *token_loss, float *lse, void *dx, float *dw,
+                            int64_t chunk, const LceWorkspace &ws, hipStream_t stream) {
+    hipError_t e;
+    if (g && V * K > 0) {
+        const int64_t n4 = V * K / 4;
+        KernelTimer timer("lce_zero_dw", stream);
+        hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, (f32x4 *)dw, n4);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const int64_t v_pad = ws.v_pad;
+    for (int64_t t0 = 0; t0 < N; t0 += chunk) {
+        const int nt = (int)(N - t0 < chunk ? N - t0 : chunk);
+        const bf16 *xc = (const bf16 *)x + (size_t)t0 * K;
+        if ((e = launch_gemm_logits(xc, nt, w, (int)V, K, ws.logits, v_pad, nt, V, stream)) != hipSuccess)
+            return e;
+        {
+            const int rows = g ? (int)round_up(nt, 64) : nt;
+            KernelTimer timer("lce_rows", stream);
+            hipLaunchKernelGGL(k_lce_rows, dim3((unsigned)rows), dim3(kThreads), 0, stream,
+                               ws.logits, v_pad, (int)V, (int)v_pad, labels + t0, ignore_index,
+                               g ? g + t0 : nullptr, nt, token_loss + t0, lse + t0,
+                               g ? (bf16 *)ws.g : nullptr, v_pad);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        if (!g) continue;
+        void *dxc = (char *)dx + (size_t)t0 * K * (dx_f32 ? 4 : 2);
+        if ((e = launch_gemm_dx(ws.g, v_pad, nt, w, (int)V, round_up(V, 64), dxc, dx_f32, K, nt,
+                                nt, stream)) != hipSuccess)
+            return e;
+        if ((e = launch_gemm_dw(ws.g, v_pad, xc, nt, round_up(nt, 64), dw, K, (int)V, V,
+                                stream)) != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}

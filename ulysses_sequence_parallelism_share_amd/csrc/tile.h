@@ -137,3 +137,25 @@ __device__ __forceinline__ bf16x8 read_tr8(const char *tile, int kbase, int m0, 
     const s16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
     return __builtin_bit_cast(bf16x8, v);
 }
+
+// The same operand with contiguous k-rows per lane: lane l supplies index
+// m0 + l % 32 and k-rows kbase + 8h + {0..7} (h = l / 32), the k-slots a
+// 16-byte read of a k-contiguous tile gives (chunk 2s + h of k16-step s), so
+// the two kinds of operand can be multiplied together.  Each 32-lane half
+// still reads 4 consecutive rows at a time (rows kbase + 8h + j/4, then
+// + 4), which keeps the swizzle's conflict-free pattern.
+template <class T>
+__device__ __forceinline__ bf16x8 read_tr8k(const char *tile, int kbase, int m0, int lane) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int G = lane >> 4, j = lane & 15;
+    const int m = m0 + 16 * (G & 1) + 4 * (j & 3);
+    const int row = kbase + 8 * (G >> 1) + (j >> 2);
+    const int c = m >> 3, sub = (m & 7) * 2;
+    const char *p0 = tile + T::off(row, c) + sub;
+    const char *p1 = tile + T::off(row + 4, c) + sub;
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds_byte *)p0);
+    const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(lds_byte *)p1);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}

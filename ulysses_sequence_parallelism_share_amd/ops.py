@@ -278,6 +278,46 @@ def sp_attn_bwd_strided(q, k, v, o, d_o, lse, position_ids, softmax_scale: float
 # Loss
 # ---------------------------------------------------------------------------
 
+def sp_linear_ce(x, w, labels, d_token_loss=None, ignore_index: int = -100,
+                 grad_dtype=torch.float32, chunk_tokens: int = 4096, out=None, ws=None):
+    """Per-token cross-entropy of x w^T (x [N][K] bf16, w [V][K] bf16, labels [N]
+    int64) without holding more than one chunk of logits.  Returns (token_loss,
+    lse) and, with d_token_loss [N] fp32, also (dx, dw fp32)."""
+    N, K = x.shape
+    V = w.shape[0]
+    _need(x, "x", _BF16)
+    _need(w, "w", _BF16, (V, K))
+    _need(labels, "labels", torch.int64, (N,))
+    if d_token_loss is not None:
+        _need(d_token_loss, "d_token_loss", torch.float32, (N,))
+    if grad_dtype == torch.float32:
+        code = _lib.SP_DTYPE_F32
+    elif grad_dtype == torch.bfloat16:
+        code = _lib.SP_DTYPE_BF16
+    else:
+        raise TypeError("grad_dtype must be torch.float32 or torch.bfloat16")
+    dev = x.device
+    if out is None:
+        out = (torch.empty(N, dtype=torch.float32, device=dev),
+               torch.empty(N, dtype=torch.float32, device=dev),
+               torch.empty((N, K), dtype=grad_dtype, device=dev) if d_token_loss is not None else None,
+               torch.empty((V, K), dtype=torch.float32, device=dev) if d_token_loss is not None else None)
+    tl, lse, dx, dw = out
+    _need(tl, "token_loss", torch.float32, (N,))
+    _need(lse, "lse", torch.float32, (N,))
+    if d_token_loss is not None:
+        _need(dx, "dx", grad_dtype, (N, K))
+        _need(dw, "dw", torch.float32, (V, K))
+    if ws is None:
+        nb = int(_lib.call("sp_linear_ce_workspace_bytes", V, chunk_tokens))
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _lib.check("sp_linear_ce", _lib.call(
+        "sp_linear_ce", _ptr(x), _ptr(w), _ptr(labels), ignore_index, _ptr(d_token_loss), N, V, K,
+        code, _ptr(tl), _ptr(lse), _ptr(dx), _ptr(dw), chunk_tokens, _ptr(ws), ws.numel(),
+        _stream()))
+    return (tl, lse) if d_token_loss is None else (tl, lse, dx, dw)
+
+
 def sp_weighted_loss(token_loss, shift_labels, ignore_index: int = -100, with_grad: bool = True,
                      out=None):
     """token_loss fp32 [P][N/P], shift_labels int64 [P][N/P] ->
