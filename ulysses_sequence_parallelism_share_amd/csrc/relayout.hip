@@ -19,7 +19,7 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 16;   // 16-byte vectors in flight per thread
 
 // One workgroup covers `rows_per_block` consecutive tokens.  Within it the
 // flat index j enumerates (token, group g, rank column q, vector w) with w
