@@ -132,7 +132,9 @@ struct DkdvSmem {
 // still in flight; PER is how many loads the wave issues per tile.
 template <int PER>
 __device__ __forceinline__ void wait_tiles(int pending) {
-    static_assert(2 * PER < 64, "vmcnt range");
+    // vmcnt(n) is encoded as 0x0F70 | n only for n < 16 (its high bits sit
+    // elsewhere in the immediate)
+    static_assert(2 * PER < 16, "vmcnt range of this encoding");
     if (pending == 0)
         __builtin_amdgcn_s_waitcnt(0x0F70);
     else if (pending == 1)
