@@ -275,7 +275,7 @@ size_t sp_linear_ce_workspace_bytes(int64_t vocab, int64_t chunk_tokens);
  *                holds that many rows of fp32 logits and bf16 G
  *   workspace    >= sp_linear_ce_workspace_bytes(vocab, chunk_tokens) bytes,
  *                256-byte aligned
- * hidden must be a positive multiple of 128 (<= 65536), else SP_E_SHAPE.
+ * hidden must be a positive multiple of 256 (<= 65536), else SP_E_SHAPE.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; fp32 log-sum-exp;
  * G rounded to bf16 for the two gradient products.  Deterministic.
  */

@@ -243,7 +243,8 @@ def _lce(**kw):
 def test_linear_ce_validation():
     ptrs = dict(x=A16, w=A16, lab=A16, tl=A16, lse=A16)
     assert _lce() == _lib.SP_E_NULL
-    assert _lce(K=200) == _lib.SP_E_SHAPE                 # hidden: multiple of 128
+    assert _lce(K=200) == _lib.SP_E_SHAPE                 # hidden: multiple of 256
+    assert _lce(K=384) == _lib.SP_E_SHAPE
     assert _lce(K=0) == _lib.SP_E_SHAPE
     assert _lce(V=0) == _lib.SP_E_SHAPE
     assert _lce(chunk=100) == _lib.SP_E_SHAPE             # chunk: multiple of 64

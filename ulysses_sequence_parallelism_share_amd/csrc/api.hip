@@ -248,8 +248,8 @@ sp_status sp_linear_ce(const void *x, const void *w, const int64_t *labels, int6
                        int grad_dtype, float *token_loss, float *lse, void *dx, float *dw,
                        int64_t chunk_tokens, void *workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-    if (n_tokens < 0 || vocab < 1 || vocab >= ((int64_t)1 << 30) || hidden < 128 ||
-        hidden % 128 != 0 || hidden > 65536 || n_tokens >= ((int64_t)1 << 31))
+    if (n_tokens < 0 || vocab < 1 || vocab >= ((int64_t)1 << 30) || hidden < 256 ||
+        hidden % 256 != 0 || hidden > 65536 || n_tokens >= ((int64_t)1 << 31))
         return SP_E_SHAPE;
     if (chunk_tokens < 64 || chunk_tokens % 64 != 0 || chunk_tokens >= ((int64_t)1 << 24))
         return SP_E_SHAPE;

@@ -7,9 +7,12 @@
 //   logits = X W^T   A = X  (k-contig)  B = W  (k-contig)
 //   dX     = G W     A = G  (k-contig)  B = W  (row-contig: k = vocab)
 //   dW    += G^T X   A = G  (row-contig: k = token)  B = X (row-contig)
-// A workgroup of 4 waves computes a 128 x 128 tile, each wave 64 x 64 as
-// 2 x 2 MFMA 32x32x16 blocks, over k-steps of 64 staged through a
-// double-buffered, XOR-swizzled LDS ring by direct global->LDS loads.  A
+// A workgroup of 8 waves computes a 256 x 256 tile, each wave 128 x 64 as
+// 4 x 2 MFMA 32x32x16 blocks, over k-steps of 64 staged through a
+// double-buffered, XOR-swizzled LDS ring by direct global->LDS loads (the
+// products are bound by moving operand tiles into LDS, so the tile is as
+// large as the LDS allows: 2 x 64 KiB, one workgroup and two waves per SIMD
+// per CU; every fragment read feeds 2 or 4 MFMAs).  A
 // k-contiguous operand is read 16 bytes per lane; a row-contiguous one with
 // the transposing LDS read that yields the same k-slots per lane.  Rows
 // past an operand's end read its last row (the caller keeps the k-range
@@ -25,18 +28,20 @@
 
 namespace {
 
-constexpr int GT = 128;      // tile rows and columns
+constexpr int GT = 256;      // tile rows and columns
 constexpr int GK = 64;       // k per step
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
 
 template <bool KC>
 struct OperandTile {
-    // k-contiguous: [128 rows][64 k]; row-contiguous: [64 k][128 rows]
-    using T = typename std::conditional<KC, SwzTile<GT, GK / 8>, SwzTile<GK, GT / 8>>::type;
-    static constexpr int kBytes = T::kBytes;
+    // k-contiguous: [256 rows][64 k]; row-contiguous: two [64 k][128 rows]
+    // halves (a swizzled tile row holds at most 256 bytes)
+    using T = typename std::conditional<KC, SwzTile<GT, GK / 8>, SwzTile<GK, GT / 16>>::type;
+    static constexpr int kParts = KC ? 1 : 2;
+    static constexpr int kBytes = kParts * T::kBytes;
     static constexpr int kRows = KC ? GT : GK;
-    static constexpr int kCh = KC ? GK / 8 : GT / 8;
+    static constexpr int kCh = KC ? GK / 8 : GT / 16;
 };
 
 template <bool KC>
@@ -45,12 +50,12 @@ __device__ __forceinline__ bf16x8 operand(const char *tile, int r0, int s, int l
     if constexpr (KC)
         return *(const bf16x8 *)(tile + T::off(r0 + (lane & 31), 2 * s + (lane >> 5)));
     else
-        return read_tr8k<T>(tile, 16 * s, r0, lane);
+        return read_tr8k<T>(tile + (r0 >> 7) * T::kBytes, 16 * s, r0 & 127, lane);
 }
 
 // OUT: 0 = store fp32, 1 = add into fp32, 2 = store bf16
 template <bool AK, bool BK, int OUT>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm(const bf16 *__restrict__ A, int64_t lda,
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(const bf16 *__restrict__ A, int64_t lda,
                                                       int a_rows, const bf16 *__restrict__ B,
                                                       int64_t ldb, int b_rows, int k_steps,
                                                       void *__restrict__ C, int64_t ldc,
@@ -67,30 +72,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const bf16 *__restrict__ A
     if (L >= m_tiles * n_tiles) return;
     const int tm = L % m_tiles, tn = L / m_tiles;
     const int m0 = tm * GT, n0 = tn * GT;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;   // wave tile rows wm*128, columns wn*64
 
     RowStager<TA::kRows, TA::kCh, kWaves> sa;
     RowStager<TB::kRows, TB::kCh, kWaves> sb;
     sa.init(wave, lane, (uint32_t)(lda * 2), 0, 0);
     sb.init(wave, lane, (uint32_t)(ldb * 2), 0, 0);
     // base and valid rows of k-step ks
+    using PA = typename TA::T;
+    using PB = typename TB::T;
     auto stage = [&](int ks, int buf) {
         char *base = smem + buf * kStage;
         const int k0 = ks * GK;
-        if constexpr (AK)
+        if constexpr (AK) {
             sa.issue(base, wave, lane, A + (size_t)m0 * lda + k0, a_rows - m0);
-        else
-            sa.issue(base, wave, lane, A + (size_t)k0 * lda + m0, GK);
-        if constexpr (BK)
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                sa.issue(base + p * PA::kBytes, wave, lane, A + (size_t)k0 * lda + m0 + 128 * p, GK);
+        }
+        if constexpr (BK) {
             sb.issue(base + TA::kBytes, wave, lane, B + (size_t)n0 * ldb + k0, b_rows - n0);
-        else
-            sb.issue(base + TA::kBytes, wave, lane, B + (size_t)k0 * ldb + n0, b_rows - k0);
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                sb.issue(base + TA::kBytes + p * PB::kBytes, wave, lane,
+                         B + (size_t)k0 * ldb + n0 + 128 * p, b_rows - k0);
+        }
     };
     stage(0, 0);
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -104,13 +118,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const bf16 *__restrict__ A
         const char *tb = ta + TA::kBytes;
 #pragma unroll
         for (int s = 0; s < GK / 16; ++s) {
-            bf16x8 a[2], b[2];
+            bf16x8 a[4], b[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = operand<AK>(ta, wm * 64 + 32 * i, s, lane);
+            for (int i = 0; i < 4; ++i) a[i] = operand<AK>(ta, wm * 128 + 32 * i, s, lane);
 #pragma unroll
             for (int j = 0; j < 2; ++j) b[j] = operand<BK>(tb, wn * 64 + 32 * j, s, lane);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
         }
@@ -119,13 +133,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(const bf16 *__restrict__ A
     // lane = column n, register r = row acc_row(r, half)
     const int half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int n = n0 + wn * 64 + 32 * j + (lane & 31);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + 32 * i + acc_row(r, half);
+                const int m = m0 + wm * 128 + 32 * i + acc_row(r, half);
                 if (m >= m_store) continue;
                 const size_t o = (size_t)m * ldc + n;
                 if constexpr (OUT == 0)
@@ -176,10 +190,15 @@ hipError_t launch_gemm_dx(const void *g, int64_t ldg, int g_rows, const void *w,
                                        m_store, M, N, stream);
 }
 
-// dW[m][n] += sum_t G[t][m] X[t][n]; G [Kt][ldg] (Kt % 64 == 0, zero rows
-// past the chunk's tokens), X [x_rows][N]; rows >= m_store not written.
+// dW[m][n] (+)= sum_t G[t][m] X[t][n] (stored for the first chunk, added for
+// the others); G [Kt][ldg] (Kt % 64 == 0, zero rows past the chunk's
+// tokens), X [x_rows][N]; rows >= m_store not written.
 hipError_t launch_gemm_dw(const void *g, int64_t ldg, const void *x, int x_rows, int64_t Kt,
-                          float *dw, int64_t N, int m_store, int64_t M, hipStream_t stream) {
-    return gemm_launch<false, false, 1>("lce_gemm_dw", g, ldg, (int)Kt, x, N, x_rows, Kt, dw, N,
+                          float *dw, int64_t N, int m_store, int64_t M, bool accumulate,
+                          hipStream_t stream) {
+    if (accumulate)
+        return gemm_launch<false, false, 1>("lce_gemm_dw", g, ldg, (int)Kt, x, N, x_rows, Kt, dw,
+                                            N, m_store, M, N, stream);
+    return gemm_launch<false, false, 0>("lce_gemm_dw", g, ldg, (int)Kt, x, N, x_rows, Kt, dw, N,
                                         m_store, M, N, stream);
 }

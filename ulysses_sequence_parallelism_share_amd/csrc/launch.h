@@ -73,7 +73,7 @@ hipError_t launch_attn_bwd(const void *q, const void *k, const void *v, const vo
 
 // Workspace of the fused linear cross-entropy: one chunk of fp32 logits and
 // of the bf16 softmax gradient, both [rows][v_pad] with v_pad = vocab rounded
-// up to 128.
+// up to 256.
 struct LceWorkspace {
     float *logits;
     void *g;

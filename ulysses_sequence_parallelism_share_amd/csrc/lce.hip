@@ -12,8 +12,9 @@
 //     G_tv   = g_t (softmax_v - [v == y_t]),  dX = G W,  dW = G^T X
 // (ignored tokens: no loss, no gradient).  Tokens are processed in chunks:
 // logits of the chunk (one GEMM), a row pass (log-sum-exp, loss and G in
-// bf16), then dX of the chunk and dW += G^T X (two GEMMs).  Only the
-// chunk's logits (fp32) and G (bf16) live in the workspace.
+// bf16), then dX of the chunk and dW (= for the first chunk, += after) G^T X
+// (two GEMMs).  Only the chunk's logits (fp32) and G (bf16) live in the
+// workspace.
 #include "common.h"
 #include "launch.h"
 
@@ -24,7 +25,8 @@ hipError_t launch_gemm_dx(const void *g, int64_t ldg, int g_rows, const void *w,
                           int64_t Kv, void *dx, bool dx_f32, int64_t N, int m_store, int64_t M,
                           hipStream_t stream);
 hipError_t launch_gemm_dw(const void *g, int64_t ldg, const void *x, int x_rows, int64_t Kt,
-                          float *dw, int64_t N, int m_store, int64_t M, hipStream_t stream);
+                          float *dw, int64_t N, int m_store, int64_t M, bool accumulate,
+                          hipStream_t stream);
 
 namespace {
 
@@ -88,17 +90,12 @@ __global__ __launch_bounds__(kThreads) void k_lce_rows(
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_fill_zero(f32x4 *__restrict__ p, int64_t n4) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i < n4) p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
 size_t lce_workspace_layout(int64_t vocab, int64_t chunk, void *base, LceWorkspace *ws) {
-    const int64_t v_pad = round_up(vocab, 128);
+    const int64_t v_pad = round_up(vocab, 256);   // the GEMM's tile width
     const size_t logits_bytes = (size_t)chunk * v_pad * 4;
     const size_t g_bytes = (size_t)round_up(chunk, 64) * v_pad * 2;
     const size_t a = (logits_bytes + 255) & ~(size_t)255;
@@ -115,13 +112,6 @@ hipError_t launch_linear_ce(const void *x, const void *w, const int64_t *labels,
                             bool dx_f32, float *token_loss, float *lse, void *dx, float *dw,
                             int64_t chunk, const LceWorkspace &ws, hipStream_t stream) {
     hipError_t e;
-    if (g && V * K > 0) {
-        const int64_t n4 = V * K / 4;
-        KernelTimer timer("lce_zero_dw", stream);
-        hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n4 + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, (f32x4 *)dw, n4);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     const int64_t v_pad = ws.v_pad;
     for (int64_t t0 = 0; t0 < N; t0 += chunk) {
         const int nt = (int)(N - t0 < chunk ? N - t0 : chunk);
@@ -142,7 +132,7 @@ hipError_t launch_linear_ce(const void *x, const void *w, const int64_t *labels,
         if ((e = launch_gemm_dx(ws.g, v_pad, nt, w, (int)V, round_up(V, 64), dxc, dx_f32, K, nt,
                                 nt, stream)) != hipSuccess)
             return e;
-        if ((e = launch_gemm_dw(ws.g, v_pad, xc, nt, round_up(nt, 64), dw, K, (int)V, V,
+        if ((e = launch_gemm_dw(ws.g, v_pad, xc, nt, round_up(nt, 64), dw, K, (int)V, V, t0 > 0,
                                 stream)) != hipSuccess)
             return e;
     }
