@@ -17,7 +17,7 @@
 //    feed dV^T += dO^T P and dK^T += Q^T dS directly; the dO^T and Q^T operands are transposing LDS
 //    reads of the same Q and dO tiles.  The GQA sum over the query heads of
 //    a KV head falls out of the virtual-row walk.
-//  * k_attn_bwd_dq - a workgroup owns 128 virtual query rows (like the
+//  * k_attn_bwd_dq - a workgroup owns 256 virtual query rows (like the
 //    forward); Q and dO stay in registers, K and V tiles stream through LDS,
 //    and dQ^T += K^T dS^T accumulates per lane (K^T by transposing reads).
 // Both stream their tiles through LDS rings filled by direct global->LDS
@@ -36,7 +36,8 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int BK = 128;  // keys per dK/dV workgroup
 constexpr int BQ = 32;   // virtual query rows per dK/dV tile
-constexpr int BM = 128;  // virtual query rows per dQ workgroup
+constexpr int BM = 256;  // virtual query rows per dQ workgroup (8 waves x 32)
+constexpr int kDqThreads = 512;
 constexpr int BN = 64;   // keys per dQ tile
 
 // ---------------------------------------------------------------------------
@@ -412,7 +413,7 @@ struct DqSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
+__global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ d_o, const float *__restrict__ rowstat,
     const int32_t *__restrict__ kstart, void *__restrict__ dq, int N, int Mpad, int hq, int hkv,
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bwd_dq(
 
     const int jt0 = key_lo / BN, jt1 = t_last / BN;
     // Keys past the end are read from the last key: finite values, always masked.
-    RowStager<BN, D / 8, kWaves> stager;
+    RowStager<BN, D / 8, kDqThreads / 64> stager;
     stager.init(wave, lane, (uint32_t)(kv_st * 2), 0, 0);
     auto stage = [&](int jt, int buf) {
         char *base = smem + buf * S::kStage;
@@ -594,7 +595,7 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
 
     const int n_row_tiles = (int)((M + BM - 1) / BM);
     KernelTimer timer("attn_bwd_dq", stream);
-    hipLaunchKernelGGL(k_attn_bwd_dq<D>, dim3((unsigned)(n_row_tiles * hkv)), dim3(kThreads), 0,
+    hipLaunchKernelGGL(k_attn_bwd_dq<D>, dim3((unsigned)(n_row_tiles * hkv)), dim3(kDqThreads), 0,
                        stream, (const bf16 *)q, (const bf16 *)k, (const bf16 *)v,
                        (const bf16 *)d_o, (const float *)ws.rowstat, (const int32_t *)ws.kstart,
                        dq, (int)N, (int)Mpad, hq, hkv, g, fg, scale_log2, scale, n_row_tiles,
