@@ -37,6 +37,7 @@ CASES = [  # name, N, hq, hkv, d, sample lengths, softmax_scale (0 = 1/sqrt(d))
     ("mha6-d64", 257, 6, 6, 64, [1, 128, 128], 0.0),
     ("custom-scale", 400, 4, 1, 128, [250, 150], 0.05),
     ("long-tile-spanning", 2100, 4, 1, 64, [2100], 0.0),
+    ("gqa3-two-kv-gathered-4k", 4096, 6, 2, 128, [1500, 1, 2595], 0.0),
 ]
 
 
