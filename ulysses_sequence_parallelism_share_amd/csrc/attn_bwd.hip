@@ -12,7 +12,7 @@
 //  * k_attn_bwd_dkdv - a workgroup owns 128 keys of one KV head (4 pairs of
 //    waves x 32 keys); K and V stay in registers as B operands, and the
 //    pairs walk the virtual query rows that can see their keys (t in
-//    [j0, segment end)) in tiles of 32, from the segment end down.
+//    [j0, segment end)) in tiles of 64, from the segment end down.
 //    S = Q K^T and dP = dO V^T come out with one key per lane, so P and dS
 //    feed dV^T += dO^T P and dK^T += Q^T dS directly; the dO^T and Q^T operands are transposing LDS
 //    reads of the same Q and dO tiles.  The GQA sum over the query heads of
@@ -35,7 +35,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int BK = 128;  // keys per dK/dV workgroup
-constexpr int BQ = 32;   // virtual query rows per dK/dV tile
+constexpr int TQ = 64;   // virtual query rows per dK/dV tile
+constexpr int RB = TQ / 32;   // its blocks of 32 rows (one MFMA row block each)
 constexpr int BM = 256;  // virtual query rows per dQ workgroup (8 waves x 32)
 constexpr int kDqThreads = 512;
 constexpr int BN = 64;   // keys per dQ tile
@@ -92,7 +93,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
 // products).  Every Q / dO fragment read from LDS feeds KPW MFMAs (one per
 // key block), so LDS traffic per MFMA falls as 1/KPW; KPW = 1 runs 8 waves,
 // two per SIMD, KPW = 2 runs 4 waves, one per SIMD, with the accumulators in
-// the accumulation registers.
+// the accumulation registers.  A query tile holds TQ = 64 rows (two row
+// blocks of 32), so the per-tile costs (barrier, load waits, ring and slot
+// bookkeeping) are paid once per 32 MFMAs of a wave; that size leaves LDS for
+// a ring of 3 tiles: B's, A's (one ahead) and one in flight.
 // ---------------------------------------------------------------------------
 // Where the query rows (Q and dO) of the dK/dV kernel's KV head come from:
 // virtual row v of KV head kh at byte offset
@@ -104,22 +108,22 @@ struct RowSource {
     int gshift, rows;
 };
 
-constexpr int kDkdvStages = 5;   // LDS ring of query tiles
-constexpr int kDkdvAhead = 3;    // tiles staged ahead of the tile B works on
+constexpr int kDkdvStages = 3;   // LDS ring of query tiles
+constexpr int kDkdvAhead = 2;    // tiles staged ahead of the tile B works on
 constexpr int kDkdvKpw = 1;      // key blocks per wave (2 needs more registers than the compiler keeps in place)
 
 template <int D, int KPW>
 struct DkdvSmem {
     static constexpr int kWaves = 8 / KPW, kPairs = kWaves / 2;
-    using R = SwzTile<BQ, D / 8>;    // Q or dO rows of the tile
-    static_assert(BQ * 8 % (kWaves * 16) == 0, "statistics split into 16-byte loads per wave");
-    static constexpr int kStatLanes = BQ * 8 / (kWaves * 16);   // 16-byte stat loads per wave
+    using R = SwzTile<TQ, D / 8>;    // Q or dO rows of the tile
+    static_assert(TQ * 8 % (kWaves * 16) == 0, "statistics split into 16-byte loads per wave");
+    static constexpr int kStatLanes = TQ * 8 / (kWaves * 16);   // 16-byte stat loads per wave
     static constexpr int kQ = 0, kDO = R::kBytes, kStat = 2 * R::kBytes;
-    static constexpr int kStage = kStat + BQ * 8;   // lse2 of BQ rows, then D of BQ rows
+    static constexpr int kStage = kStat + TQ * 8;   // per 32-row block: lse2 of 32 rows, then D
     // P handed from A to B: [2 slots][pair][key block][2 halves][64 lanes] x
     // 16 bytes (a 16-byte lane stride keeps the exchange bank-conflict free)
     static constexpr int kP = kDkdvStages * kStage;
-    static constexpr int kPSlot = kPairs * KPW * 2 * 64 * 16;
+    static constexpr int kPSlot = kPairs * KPW * RB * 2 * 64 * 16;
     static constexpr int kBytes = kP + 2 * kPSlot;
     // direct loads per wave per tile: its share of the Q and dO rows, plus statistics
     __device__ static constexpr int loads(int wave) {
@@ -174,19 +178,19 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
         my_kend[b] = kend[key[b] < N ? key[b] : N - 1];
     }
 
-    // Rows [j0*g, kend_max*g) can see these keys; j0*g is a multiple of BQ.
+    // Rows [j0*g, kend_max*g) can see these keys; j0*g is a multiple of TQ.
     const int vq_lo = j0 * g;
-    const int n_it = (kend_max * g - vq_lo + BQ - 1) / BQ;
+    const int n_it = (kend_max * g - vq_lo + TQ - 1) / TQ;
     // Tiles are walked from the end of the range down to the diagonal: key
     // tiles of one sample share that end, so workgroups running side by side
     // read the same Q and dO rows at about the same time and share them in L2.
-    auto tile_row = [&](int it) { return vq_lo + (n_it - 1 - it) * BQ; };
+    auto tile_row = [&](int it) { return vq_lo + (n_it - 1 - it) * TQ; };
     // Virtual row v of KV head kh lies at byte offset kh * head_bytes +
     // (v >> gshift) * tok_bytes + (v & (2^gshift - 1)) * D * 2 of q_rows /
     // do_rows (`RowSource`); tiles start at multiples of 32 rows, hence at
     // token boundaries.  Rows past the end are read from the last row: finite
     // data, and their statistics make P exactly 0.
-    RowStager<BQ, D / 8, W> stager_q, stager_do;
+    RowStager<TQ, D / 8, W> stager_q, stager_do;
     stager_q.init(wave, lane, rs.q_tok_bytes, D * 2, rs.gshift);
     stager_do.init(wave, lane, rs.do_tok_bytes, D * 2, rs.gshift);
     const char *q_head = (const char *)q_rows + (size_t)kh * rs.q_head_bytes;
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
     auto advance = [](int x) { return x + 1 == kDkdvStages ? 0 : x + 1; };
     // Iteration -1 runs A on tile 0 only; iteration it runs A on it+1, B on it.
     for (int it = -1; it < n_it; ++it) {
-        if (it >= 0) wait_for(it + 2 < n_it ? 1 : 0);   // tile it+1 for A
+        if (it >= 0) wait_for(max(0, min(kDkdvAhead - 2, n_it - 2 - it)));   // tile it+1 for A
         __syncthreads();
         if (it >= 0 && it + kDkdvAhead < n_it) {
             slot_st = advance(slot_st);
@@ -288,78 +292,93 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
         if (t < 0 || t >= n_it) continue;
         const char *base = smem + slot * S::kStage;
         const int vq0 = tile_row(t);
-        const float *stat = (const float *)(base + S::kStat);   // lse2 of BQ rows, then D
-        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot) + pair * KPW * 128 + lane;
+        const float *stat = (const float *)(base + S::kStat);   // per row block: lse2 of 32 rows, then D
+        // P slot: [pair][key block][row block][2 halves][64 lanes]
+        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot) + pair * KPW * RB * 128 + lane;
 
         // First product: S = Q K^T (A) or dP = dO V^T (B); lane = key.
-        f32x16 x[KPW];
+        f32x16 x[RB][KPW];
 #pragma unroll
-        for (int b = 0; b < KPW; ++b)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[b][r] = 0.f;
+            for (int b = 0; b < KPW; ++b)
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const bf16x8 a = *(const bf16x8 *)(base + rows1 + S::R::off(col, 2 * st + half));
+                for (int r = 0; r < 16; ++r) x[rb][b][r] = 0.f;
 #pragma unroll
-            for (int b = 0; b < KPW; ++b) x[b] = mfma32(a, kv[b][st], x[b]);
-        }
+        for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const bf16x8 a = *(const bf16x8 *)(base + rows1 + S::R::off(rb * 32 + col, 2 * st + half));
+#pragma unroll
+                for (int b = 0; b < KPW; ++b) x[rb][b] = mfma32(a, kv[b][st], x[rb][b]);
+            }
 
         // rows of accumulator register r: rg*8 + half*4 + i (r = rg*4 + i)
-        bf16x8 opnd[KPW][2];
+        bf16x8 opnd[KPW][RB][2];
         if (role_a) {
-            const int tq_first = (int)fdiv((uint32_t)vq0, fg);
-            const int tq_last = (int)fdiv((uint32_t)(min(vq0 + BQ, M) - 1), fg);
-            // A pair whose pairs are all masked still runs (its P is exactly
-            // 0); that happens only on the diagonal and at sample ends.
-            const bool full = pair_has_keys && (kw1 <= tq_first) && (tq_last < kend_w0);
-            auto softmax = [&](auto masked) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int vb = vq0 + rb * 32;
+                const float *l2s = stat + rb * 64;
+                const int tq_first = (int)fdiv((uint32_t)min(vb, M - 1), fg);
+                const int tq_last = (int)fdiv((uint32_t)(min(vb + 32, M) - 1), fg);
+                // A pair whose pairs are all masked still runs (its P is exactly
+                // 0); that happens only on the diagonal and at sample ends.
+                const bool full = pair_has_keys && vb < M && (kw1 <= tq_first) && (tq_last < kend_w0);
+                auto softmax = [&](auto masked) {
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int q0 = rg * 8 + half * 4;
+                        const f32x4 l2 = *(const f32x4 *)(l2s + q0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = rg * 4 + i;
+                            int tq = 0;
+                            if constexpr (decltype(masked)::value)
+                                tq = (int)fdiv((uint32_t)(vb + q0 + i), fg);
+#pragma unroll
+                            for (int b = 0; b < KPW; ++b) {
+                                float p = fast_exp2(fmaf(x[rb][b][r], scale_log2, -l2[i]));
+                                if constexpr (decltype(masked)::value)
+                                    p = (key[b] <= tq && tq < my_kend[b]) ? p : 0.f;
+                                opnd[b][rb][r >> 3][r & 7] = (bf16)p;
+                            }
+                        }
+                    }
+                };
+                if (full)
+                    softmax(std::false_type{});
+                else
+                    softmax(std::true_type{});
+            }
+#pragma unroll
+            for (int b = 0; b < KPW; ++b)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    ps[(b * RB + rb) * 128] = opnd[b][rb][0];
+                    ps[(b * RB + rb) * 128 + 64] = opnd[b][rb][1];
+                }
+        } else {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                bf16x8 pb[KPW][2];
+#pragma unroll
+                for (int b = 0; b < KPW; ++b) {
+                    pb[b][0] = ps[(b * RB + rb) * 128];
+                    pb[b][1] = ps[(b * RB + rb) * 128 + 64];
+                }
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int q0 = rg * 8 + half * 4;
-                    const f32x4 l2 = *(const f32x4 *)(stat + q0);
+                    const f32x4 dl = *(const f32x4 *)(stat + rb * 64 + 32 + q0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = rg * 4 + i;
-                        int tq = 0;
-                        if constexpr (decltype(masked)::value)
-                            tq = (int)fdiv((uint32_t)(vq0 + q0 + i), fg);
 #pragma unroll
                         for (int b = 0; b < KPW; ++b) {
-                            float p = fast_exp2(fmaf(x[b][r], scale_log2, -l2[i]));
-                            if constexpr (decltype(masked)::value)
-                                p = (key[b] <= tq && tq < my_kend[b]) ? p : 0.f;
-                            opnd[b][r >> 3][r & 7] = (bf16)p;
+                            const float p = (float)pb[b][r >> 3][r & 7];
+                            opnd[b][rb][r >> 3][r & 7] = (bf16)(p * (x[rb][b][r] - dl[i]));
                         }
-                    }
-                }
-            };
-            if (full)
-                softmax(std::false_type{});
-            else
-                softmax(std::true_type{});
-#pragma unroll
-            for (int b = 0; b < KPW; ++b) {
-                ps[b * 128] = opnd[b][0];
-                ps[b * 128 + 64] = opnd[b][1];
-            }
-        } else {
-            bf16x8 pb[KPW][2];
-#pragma unroll
-            for (int b = 0; b < KPW; ++b) {
-                pb[b][0] = ps[b * 128];
-                pb[b][1] = ps[b * 128 + 64];
-            }
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int q0 = rg * 8 + half * 4;
-                const f32x4 dl = *(const f32x4 *)(stat + BQ + q0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = rg * 4 + i;
-#pragma unroll
-                    for (int b = 0; b < KPW; ++b) {
-                        const float p = (float)pb[b][r >> 3][r & 7];
-                        opnd[b][r >> 3][r & 7] = (bf16)(p * (x[b][r] - dl[i]));
                     }
                 }
             }
@@ -369,10 +388,11 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
+            for (int s2 = 0; s2 < 2 * RB; ++s2) {
                 const bf16x8 a = tr_read(base + rows2, db, 16 * s2);
 #pragma unroll
-                for (int b = 0; b < KPW; ++b) acc[b][db] = mfma32(a, opnd[b][s2], acc[b][db]);
+                for (int b = 0; b < KPW; ++b)
+                    acc[b][db] = mfma32(a, opnd[b][s2 >> 1][s2 & 1], acc[b][db]);
             }
     }
 
