@@ -120,7 +120,7 @@ struct DkdvSmem {
     static constexpr int kStatLanes = TQ * 8 / (kWaves * 16);   // 16-byte stat loads per wave
     static constexpr int kQ = 0, kDO = R::kBytes, kStat = 2 * R::kBytes;
     static constexpr int kStage = kStat + TQ * 8;   // per 32-row block: lse2 of 32 rows, then D
-    // P handed from A to B: [2 slots][pair][key block][2 halves][64 lanes] x
+    // P handed from A to B: [2 slots][pair][key block][row block][2 halves][64 lanes] x
     // 16 bytes (a 16-byte lane stride keeps the exchange bank-conflict free)
     static constexpr int kP = kDkdvStages * kStage;
     static constexpr int kPSlot = kPairs * KPW * RB * 2 * 64 * 16;
@@ -304,14 +304,27 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
             for (int b = 0; b < KPW; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) x[rb][b][r] = 0.f;
+        // The row fragments are read PF ahead of the MFMA that takes them
+        // (sched_group_barrier pins that order: the compiler would otherwise
+        // wait for each read right before its MFMA).
+        {
+            constexpr int NFR = (D / 16) * RB, PF = 6;
+            bf16x8 fa[NFR];
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st)
+            for (int f = 0; f < NFR; ++f)
+                fa[f] = *(const bf16x8 *)(base + rows1 + S::R::off((f % RB) * 32 + col, 2 * (f / RB) + half));
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const bf16x8 a = *(const bf16x8 *)(base + rows1 + S::R::off(rb * 32 + col, 2 * st + half));
+            for (int f = 0; f < NFR; ++f)
 #pragma unroll
-                for (int b = 0; b < KPW; ++b) x[rb][b] = mfma32(a, kv[b][st], x[rb][b]);
+                for (int b = 0; b < KPW; ++b) x[f % RB][b] = mfma32(fa[f], kv[b][f / RB], x[f % RB][b]);
+            __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+            for (int f = 0; f < NFR - PF; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+        }
 
         // rows of accumulator register r: rg*8 + half*4 + i (r = rg*4 + i)
         bf16x8 opnd[KPW][RB][2];
@@ -385,15 +398,28 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
         }
 
         // Second product: dV^T += dO^T P (A) or dK^T += Q^T dS (B).
+        // Transposed fragments f = s2 * D/32 + db, read PF2 ahead; each
+        // accumulator still sums its k-rows in ascending order.
+        {
+            constexpr int NF2 = (D / 32) * 2 * RB, PF2 = 4;
+            bf16x8 fb[NF2];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int f = 0; f < NF2; ++f) fb[f] = tr_read(base + rows2, f % (D / 32), 16 * (f / (D / 32)));
 #pragma unroll
-            for (int s2 = 0; s2 < 2 * RB; ++s2) {
-                const bf16x8 a = tr_read(base + rows2, db, 16 * s2);
+            for (int f = 0; f < NF2; ++f) {
+                const int db = f % (D / 32), s2 = f / (D / 32);
 #pragma unroll
                 for (int b = 0; b < KPW; ++b)
-                    acc[b][db] = mfma32(a, opnd[b][s2 >> 1][s2 & 1], acc[b][db]);
+                    acc[b][db] = mfma32(fb[f], opnd[b][s2 >> 1][s2 & 1], acc[b][db]);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF2, 1);
+#pragma unroll
+            for (int f = 0; f < NF2 - PF2; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, PF2, 1);
+        }
     }
 
     void *out = role_a ? dv : dk;
