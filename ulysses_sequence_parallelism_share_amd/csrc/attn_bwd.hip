@@ -33,7 +33,6 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int BK = 128;  // keys per dK/dV workgroup
 constexpr int TQ = 64;   // virtual query rows per dK/dV tile
 constexpr int RB = TQ / 32;   // its blocks of 32 rows (one MFMA row block each)
@@ -84,16 +83,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_rowstats(const bf16 *__restric
 // ---------------------------------------------------------------------------
 // dK, dV
 //
-// A workgroup owns BK = 128 keys of one KV head, split over wave pairs; a
-// pair owns 32*KPW keys (KPW key blocks of 32).  Wave "A" of a pair holds K
+// A workgroup owns BK = 128 keys of one KV head, split over 4 wave pairs of
+// 32 keys; 8 waves, two per SIMD.  Wave "A" of a pair holds K
 // and accumulates dV: S = Q K^T, P, then dV^T += dO^T P.  Wave "B" holds V
 // and accumulates dK: dP = dO V^T, then, with P from A, dS = P * (dP - D)
 // and dK^T += Q^T dS.  A hands P to B through LDS in bf16, lane for lane in
 // the accumulator layout both waves share (S and dP are both [rows x keys]
-// products).  Every Q / dO fragment read from LDS feeds KPW MFMAs (one per
-// key block), so LDS traffic per MFMA falls as 1/KPW; KPW = 1 runs 8 waves,
-// two per SIMD, KPW = 2 runs 4 waves, one per SIMD, with the accumulators in
-// the accumulation registers.  A query tile holds TQ = 64 rows (two row
+// products).  Every Q / dO fragment read from LDS feeds one MFMA (two key
+// blocks per wave would halve that traffic but need more registers than
+// two waves per SIMD leave).  A query tile holds TQ = 64 rows (two row
 // blocks of 32), so the per-tile costs (barrier, load waits, ring and slot
 // bookkeeping) are paid once per 32 MFMAs of a wave; that size leaves LDS for
 // a ring of 3 tiles: B's, A's (one ahead) and one in flight.
@@ -110,20 +108,19 @@ struct RowSource {
 
 constexpr int kDkdvStages = 3;   // LDS ring of query tiles
 constexpr int kDkdvAhead = 2;    // tiles staged ahead of the tile B works on
-constexpr int kDkdvKpw = 1;      // key blocks per wave (2 needs more registers than the compiler keeps in place)
 
-template <int D, int KPW>
+template <int D>
 struct DkdvSmem {
-    static constexpr int kWaves = 8 / KPW, kPairs = kWaves / 2;
+    static constexpr int kWaves = 8, kPairs = 4;
     using R = SwzTile<TQ, D / 8>;    // Q or dO rows of the tile
     static_assert(TQ * 8 % (kWaves * 16) == 0, "statistics split into 16-byte loads per wave");
     static constexpr int kStatLanes = TQ * 8 / (kWaves * 16);   // 16-byte stat loads per wave
     static constexpr int kQ = 0, kDO = R::kBytes, kStat = 2 * R::kBytes;
     static constexpr int kStage = kStat + TQ * 8;   // per 32-row block: lse2 of 32 rows, then D
-    // P handed from A to B: [2 slots][pair][key block][row block][2 halves][64 lanes] x
+    // P handed from A to B: [2 slots][pair][row block][2 halves][64 lanes] x
     // 16 bytes (a 16-byte lane stride keeps the exchange bank-conflict free)
     static constexpr int kP = kDkdvStages * kStage;
-    static constexpr int kPSlot = kPairs * KPW * RB * 2 * 64 * 16;
+    static constexpr int kPSlot = kPairs * RB * 2 * 64 * 16;
     static constexpr int kBytes = kP + 2 * kPSlot;
     // direct loads per wave per tile: its share of the Q and dO rows, plus statistics
     __device__ static constexpr int loads(int wave) {
@@ -148,14 +145,14 @@ __device__ __forceinline__ void wait_tiles(int pending) {
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER));
 }
 
-template <int D, int KPW>
-__global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
+template <int D>
+__global__ __launch_bounds__(512, 1) void k_attn_bwd_dkdv(
     const bf16 *__restrict__ k, const bf16 *__restrict__ v, const bf16 *__restrict__ q_rows,
     const bf16 *__restrict__ do_rows, RowSource rs, const float *__restrict__ rowstat,
     const int32_t *__restrict__ kend, void *__restrict__ dk, void *__restrict__ dv, int N,
     int Mpad, int hkv, int g, FastDiv fg, float scale_log2, float scale, int out_f32,
     int64_t kv_st, int64_t dk_st, int64_t dv_st) {
-    using S = DkdvSmem<D, KPW>;
+    using S = DkdvSmem<D>;
     constexpr int W = S::kWaves, PAIRS = S::kPairs;
     __shared__ __attribute__((aligned(1024))) char smem[S::kBytes];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -166,17 +163,13 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
     const int kh = blockIdx.x % hkv;
     const int j0 = (blockIdx.x / hkv) * BK;
     const int M = N * g;
-    const int kw0 = j0 + pair * 32 * KPW;               // the pair's first key
-    const int kw1 = min(kw0 + 32 * KPW - 1, N - 1);     // and last (if kw0 < N)
+    const int kw0 = j0 + pair * 32;               // the pair's first key
+    const int kw1 = min(kw0 + 31, N - 1);         // and last (if kw0 < N)
     const bool pair_has_keys = kw0 < N;
     const int kend_w0 = pair_has_keys ? kend[kw0] : 0;
     const int kend_max = kend[min(j0 + BK, N) - 1];
-    int key[KPW], my_kend[KPW];
-#pragma unroll
-    for (int b = 0; b < KPW; ++b) {
-        key[b] = kw0 + 32 * b + col;
-        my_kend[b] = kend[key[b] < N ? key[b] : N - 1];
-    }
+    const int key = kw0 + col;                    // this lane's key
+    const int my_kend = kend[key < N ? key : N - 1];
 
     // Rows [j0*g, kend_max*g) can see these keys; j0*g is a multiple of TQ.
     const int vq_lo = j0 * g;
@@ -209,13 +202,12 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
     };
     for (int i = 0; i < kDkdvAhead && i < n_it; ++i) stage(i, i);
 
-    // This wave's B operands (K for A, V for B), lane = key.
-    bf16x8 kv[KPW][D / 16];
-#pragma unroll
-    for (int b = 0; b < KPW; ++b) {
+    // This wave's B operand (K for A, V for B), lane = key.
+    bf16x8 kv[D / 16];
+    {
         const bf16 *src = role_a ? k : v;
-        const bool ok = key[b] < N;
-        const size_t off = (size_t)(ok ? key[b] : 0) * kv_st + kh * D + half * 8;
+        const bool ok = key < N;
+        const size_t off = (size_t)(ok ? key : 0) * kv_st + kh * D + half * 8;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
             bf16x8 a = *(const bf16x8 *)(src + off + 16 * st);
@@ -223,16 +215,14 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
 #pragma unroll
                 for (int i = 0; i < 8; ++i) a[i] = (bf16)0.f;
             }
-            kv[b][st] = a;
+            kv[st] = a;
         }
     }
-    f32x16 acc[KPW][D / 32];   // dV^T (A) or dK^T (B): lane = key, registers = features
+    f32x16 acc[D / 32];   // dV^T (A) or dK^T (B): lane = key, registers = features
 #pragma unroll
-    for (int b = 0; b < KPW; ++b)
+    for (int i = 0; i < D / 32; ++i)
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[b][i][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
     // A runs one tile ahead of B: in iteration `it`, A turns tile it+1 into P
     // (double-buffered exchange slot) and dV, while B turns tile it and A's P
@@ -293,17 +283,15 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
         const char *base = smem + slot * S::kStage;
         const int vq0 = tile_row(t);
         const float *stat = (const float *)(base + S::kStat);   // per row block: lse2 of 32 rows, then D
-        // P slot: [pair][key block][row block][2 halves][64 lanes]
-        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot) + pair * KPW * RB * 128 + lane;
+        // P slot: [pair][row block][2 halves][64 lanes]
+        bf16x8 *ps = (bf16x8 *)(smem + S::kP + (t & 1) * S::kPSlot) + pair * RB * 128 + lane;
 
         // First product: S = Q K^T (A) or dP = dO V^T (B); lane = key.
-        f32x16 x[RB][KPW];
+        f32x16 x[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int b = 0; b < KPW; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[rb][b][r] = 0.f;
+            for (int r = 0; r < 16; ++r) x[rb][r] = 0.f;
         // The row fragments are read PF ahead of the MFMA that takes them
         // (sched_group_barrier pins that order: the compiler would otherwise
         // wait for each read right before its MFMA).
@@ -314,9 +302,7 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
             for (int f = 0; f < NFR; ++f)
                 fa[f] = *(const bf16x8 *)(base + rows1 + S::R::off((f % RB) * 32 + col, 2 * (f / RB) + half));
 #pragma unroll
-            for (int f = 0; f < NFR; ++f)
-#pragma unroll
-                for (int b = 0; b < KPW; ++b) x[f % RB][b] = mfma32(fa[f], kv[b][f / RB], x[f % RB][b]);
+            for (int f = 0; f < NFR; ++f) x[f % RB] = mfma32(fa[f], kv[f / RB], x[f % RB]);
             __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
             for (int f = 0; f < NFR - PF; ++f) {
@@ -327,7 +313,7 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
         }
 
         // rows of accumulator register r: rg*8 + half*4 + i (r = rg*4 + i)
-        bf16x8 opnd[KPW][RB][2];
+        bf16x8 opnd[RB][2];
         if (role_a) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -349,13 +335,10 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
                             int tq = 0;
                             if constexpr (decltype(masked)::value)
                                 tq = (int)fdiv((uint32_t)(vb + q0 + i), fg);
-#pragma unroll
-                            for (int b = 0; b < KPW; ++b) {
-                                float p = fast_exp2(fmaf(x[rb][b][r], scale_log2, -l2[i]));
-                                if constexpr (decltype(masked)::value)
-                                    p = (key[b] <= tq && tq < my_kend[b]) ? p : 0.f;
-                                opnd[b][rb][r >> 3][r & 7] = (bf16)p;
-                            }
+                            float p = fast_exp2(fmaf(x[rb][r], scale_log2, -l2[i]));
+                            if constexpr (decltype(masked)::value)
+                                p = (key <= tq && tq < my_kend) ? p : 0.f;
+                            opnd[rb][r >> 3][r & 7] = (bf16)p;
                         }
                     }
                 };
@@ -365,21 +348,14 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
                     softmax(std::true_type{});
             }
 #pragma unroll
-            for (int b = 0; b < KPW; ++b)
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    ps[(b * RB + rb) * 128] = opnd[b][rb][0];
-                    ps[(b * RB + rb) * 128 + 64] = opnd[b][rb][1];
-                }
+            for (int rb = 0; rb < RB; ++rb) {
+                ps[rb * 128] = opnd[rb][0];
+                ps[rb * 128 + 64] = opnd[rb][1];
+            }
         } else {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                bf16x8 pb[KPW][2];
-#pragma unroll
-                for (int b = 0; b < KPW; ++b) {
-                    pb[b][0] = ps[(b * RB + rb) * 128];
-                    pb[b][1] = ps[(b * RB + rb) * 128 + 64];
-                }
+                const bf16x8 pb[2] = {ps[rb * 128], ps[rb * 128 + 64]};
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int q0 = rg * 8 + half * 4;
@@ -387,11 +363,8 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = rg * 4 + i;
-#pragma unroll
-                        for (int b = 0; b < KPW; ++b) {
-                            const float p = (float)pb[b][r >> 3][r & 7];
-                            opnd[b][rb][r >> 3][r & 7] = (bf16)(p * (x[rb][b][r] - dl[i]));
-                        }
+                        const float p = (float)pb[r >> 3][r & 7];
+                        opnd[rb][r >> 3][r & 7] = (bf16)(p * (x[rb][r] - dl[i]));
                     }
                 }
             }
@@ -408,9 +381,7 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
 #pragma unroll
             for (int f = 0; f < NF2; ++f) {
                 const int db = f % (D / 32), s2 = f / (D / 32);
-#pragma unroll
-                for (int b = 0; b < KPW; ++b)
-                    acc[b][db] = mfma32(fb[f], opnd[b][s2 >> 1][s2 & 1], acc[b][db]);
+                acc[db] = mfma32(fb[f], opnd[s2 >> 1][s2 & 1], acc[db]);
             }
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF2, 1);
 #pragma unroll
@@ -422,30 +393,27 @@ __global__ __launch_bounds__(64 * 8 / KPW, 1) void k_attn_bwd_dkdv(
         }
     }
 
+    if (key >= N) return;
     void *out = role_a ? dv : dk;
     const float mul = role_a ? 1.f : scale;
+    const size_t obase = (size_t)key * (role_a ? dv_st : dk_st) + kh * D;
 #pragma unroll
-    for (int b = 0; b < KPW; ++b) {
-        if (key[b] >= N) continue;
-        const size_t obase = (size_t)key[b] * (role_a ? dv_st : dk_st) + kh * D;
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int rg = 0; rg < 4; ++rg) {
+            const int e = db * 32 + rg * 8 + half * 4;
+            if (out_f32) {
+                f32x4 a;
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int e = db * 32 + rg * 8 + half * 4;
-                if (out_f32) {
-                    f32x4 a;
+                for (int i = 0; i < 4; ++i) a[i] = acc[db][rg * 4 + i] * mul;
+                *(f32x4 *)((float *)out + obase + e) = a;
+            } else {
+                bf16x4 a;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) a[i] = acc[b][db][rg * 4 + i] * mul;
-                    *(f32x4 *)((float *)out + obase + e) = a;
-                } else {
-                    bf16x4 a;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a[i] = (bf16)(acc[b][db][rg * 4 + i] * mul);
-                    *(bf16x4 *)((bf16 *)out + obase + e) = a;
-                }
+                for (int i = 0; i < 4; ++i) a[i] = (bf16)(acc[db][rg * 4 + i] * mul);
+                *(bf16x4 *)((bf16 *)out + obase + e) = a;
             }
-    }
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -631,8 +599,8 @@ hipError_t bwd_launch(const void *q, const void *k, const void *v, const void *o
     {
         const int n_key_tiles = (int)((N + BK - 1) / BK);
         KernelTimer timer("attn_bwd_dkdv", stream);
-        hipLaunchKernelGGL((k_attn_bwd_dkdv<D, kDkdvKpw>), dim3((unsigned)(n_key_tiles * hkv)),
-                           dim3(64 * 8 / kDkdvKpw), 0, stream, (const bf16 *)k, (const bf16 *)v,
+        hipLaunchKernelGGL((k_attn_bwd_dkdv<D>), dim3((unsigned)(n_key_tiles * hkv)),
+                           dim3(512), 0, stream, (const bf16 *)k, (const bf16 *)v,
                            q_rows, do_rows, rs, (const float *)ws.rowstat,
                            (const int32_t *)ws.kend, dk, dv, (int)N, (int)Mpad, hkv, g, fg,
                            scale_log2, scale, (int)grad_f32, st.k, st.dk, st.dv);
