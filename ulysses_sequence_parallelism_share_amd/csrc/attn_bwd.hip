@@ -38,7 +38,7 @@ constexpr int TQ = 64;   // virtual query rows per dK/dV tile
 constexpr int RB = TQ / 32;   // its blocks of 32 rows (one MFMA row block each)
 constexpr int BM = 256;  // virtual query rows per dQ workgroup (8 waves x 32)
 constexpr int kDqThreads = 512;
-constexpr int BN = 64;   // keys per dQ tile
+constexpr int BN = 128;  // keys per dQ tile
 
 // ---------------------------------------------------------------------------
 // Row statistics of virtual row v < Mpad of KV head kh, in blocks of 32 rows:
@@ -494,9 +494,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_attn_bwd_dq(
         const char *base = smem + ((jt - jt0) & 1) * S::kStage;
 
         // One 32-key block at a time: S^T and dP^T, then dS^T, then its part
-        // of dQ^T (keeps half the score registers live).
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        // of dQ^T (keeps the score registers of one block live; unrolled by
+        // two, which the register budget still holds without spilling).
+#pragma unroll 2
+        for (int kb = 0; kb < BN / 32; ++kb) {
             f32x16 s, dp;
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
