@@ -32,45 +32,68 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ float block_reduce(float x, float *red, bool is_max) {
+// Block-wide log-sum-exp in the log2 domain: each thread brings a running
+// max m and a sum s of 2^(x - m); pairs combine as
+// (max(m1, m2), s1 2^(m1 - m) + s2 2^(m2 - m)).
+__device__ __forceinline__ void lse_combine(float &m, float &s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;   // both empty
+    s = s * fast_exp2(m - mn) + s2 * fast_exp2(m2 - mn);
+    m = mn;
+}
+
+__device__ __forceinline__ void block_lse(float &m, float &s, float2 *red) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float y = __shfl_xor(x, o);
-        x = is_max ? fmaxf(x, y) : x + y;
-    }
+    for (int o = 32; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
     const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = make_float2(m, s);
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = x;
-    __syncthreads();
-    float r = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
-    return r;
+    m = red[0].x;
+    s = red[0].y;
+    for (int i = 1; i < kThreads / 64; ++i) lse_combine(m, s, red[i].x, red[i].y);
 }
 
 // One workgroup per token row of the chunk (rows at or past n_tok only
 // clear their G row, so the dW product's padded k-range adds nothing).
 // Labels outside [0, V) other than ignore_index give a NaN loss and no
-// gradient.
+// gradient.  The row is read twice: once for its log-sum-exp (running max
+// and rescaled sum, in 16-byte pieces), once for G.
 __global__ __launch_bounds__(kThreads) void k_lce_rows(
     const float *__restrict__ logits, int64_t ldl, int V, int v_pad,
     const int64_t *__restrict__ labels, int64_t ignore_index, const float *__restrict__ g,
     int n_tok, float *__restrict__ token_loss, float *__restrict__ lse_out,
     bf16 *__restrict__ G, int64_t ldg) {
-    __shared__ float red[kThreads / 64];
+    __shared__ float2 red[kThreads / 64];
     const int row = blockIdx.x;
+    const int n4 = v_pad / 4;   // v_pad is a multiple of 256
     if (row >= n_tok) {
-        if (G)
-            for (int v = threadIdx.x; v < v_pad; v += kThreads) G[(size_t)row * ldg + v] = (bf16)0.f;
+        if (G) {
+            bf16x4 z;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) z[e] = (bf16)0.f;
+            for (int c = threadIdx.x; c < n4; c += kThreads) *((bf16x4 *)(G + (size_t)row * ldg) + c) = z;
+        }
         return;
     }
     const float *l = logits + (size_t)row * ldl;
-    float mx = -INFINITY;
-    for (int v = threadIdx.x; v < V; v += kThreads) mx = fmaxf(mx, l[v]);
-    mx = block_reduce(mx, red, true);
-    float s = 0.f;
-    for (int v = threadIdx.x; v < V; v += kThreads) s += fast_exp2((l[v] - mx) * SP_LOG2E);
-    s = block_reduce(s, red, false);
-    const float lse = mx + __logf(s);
+    float m = -INFINITY, sum = 0.f;   // log2 domain
+    for (int c = threadIdx.x; c < n4; c += kThreads) {
+        const f32x4 x = *((const f32x4 *)l + c);
+        float y[4], cm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            y[e] = 4 * c + e < V ? x[e] * SP_LOG2E : -INFINITY;
+            cm = fmaxf(cm, y[e]);
+        }
+        if (cm == -INFINITY) continue;   // past the vocabulary
+        const float mn = fmaxf(m, cm);
+        sum *= fast_exp2(m - mn);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum += fast_exp2(y[e] - mn);
+        m = mn;
+    }
+    block_lse(m, sum, red);
+    const float lse = (m + __log2f(sum)) * SP_LN2;
     const int64_t y = labels[row];
     const bool ignored = y == ignore_index;
     const bool in_range = y >= 0 && y < V;
@@ -82,11 +105,18 @@ __global__ __launch_bounds__(kThreads) void k_lce_rows(
     if (!G) return;
     const float gt = valid ? g[row] : 0.f;
     const float sh = lse * SP_LOG2E;
-    bf16 *gr = G + (size_t)row * ldg;
-    for (int v = threadIdx.x; v < v_pad; v += kThreads) {
-        float x = 0.f;
-        if (v < V) x = gt * (fast_exp2(fmaf(l[v], SP_LOG2E, -sh)) - (v == y ? 1.f : 0.f));
-        gr[v] = (bf16)x;
+    bf16x4 *gr = (bf16x4 *)(G + (size_t)row * ldg);
+    for (int c = threadIdx.x; c < n4; c += kThreads) {
+        const f32x4 x = *((const f32x4 *)l + c);
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int v = 4 * c + e;
+            float p = 0.f;
+            if (v < V) p = gt * (fast_exp2(fmaf(x[e], SP_LOG2E, -sh)) - (v == y ? 1.f : 0.f));
+            o[e] = (bf16)p;
+        }
+        gr[c] = o;
     }
 }
 
