@@ -28,6 +28,14 @@
 
 namespace {
 
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
 constexpr int GT = 256;      // tile rows and columns
 constexpr int GK = 64;       // k per step
 constexpr int kThreads = 512;
@@ -116,17 +124,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const bf16 *__restrict__ A
         if (ks + 1 < k_steps) stage(ks + 1, (ks + 1) & 1);
         const char *ta = smem + (ks & 1) * kStage;
         const char *tb = ta + TA::kBytes;
+        bf16x8 a[GK / 16][4], b[GK / 16][2];
 #pragma unroll
         for (int s = 0; s < GK / 16; ++s) {
-            bf16x8 a[4], b[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = operand<AK>(ta, wm * 128 + 32 * i, s, lane);
+            for (int i = 0; i < 4; ++i) a[s][i] = operand<AK>(ta, wm * 128 + 32 * i, s, lane);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = operand<BK>(tb, wn * 64 + 32 * j, s, lane);
+            for (int j = 0; j < 2; ++j) b[s][j] = operand<BK>(tb, wn * 64 + 32 * j, s, lane);
+        }
+#pragma unroll
+        for (int s = 0; s < GK / 16; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[s][i], b[s][j], acc[i][j]);
+        // The fragments of k16 step s+1 are read while step s multiplies
+        // (sched_group_barrier pins that interleave; left alone the compiler
+        // waits for each step's reads before its MFMAs).
+        {
+            constexpr int RD = (AK ? 1 : 2) * 4 + (BK ? 1 : 2) * 2;   // LDS reads per k16 step
+            __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+#pragma unroll
+            for (int s = 0; s + 1 < GK / 16; ++s) {
+                static_for<0, 8>([&](auto m) {
+                    constexpr int M = decltype(m)::value;
+                    constexpr int nr = RD * (M + 1) / 8 - RD * M / 8;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+                });
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
     }
 
