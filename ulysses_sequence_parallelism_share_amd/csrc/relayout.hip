@@ -73,7 +73,10 @@ hipError_t launch_relayout(bool to_head, const void *src, void *dst, int P, int6
     const uint32_t nq = rank < 0 ? (uint32_t)P : 1u;        // pieces per (token, group)
     const uint32_t R = (uint32_t)G * nq * W;                // vectors per token
     const uint32_t HW = (uint32_t)H * (uint32_t)d / 8;      // vectors per (token, group) row
-    uint32_t rows = 8192u / R;
+    // About 2048 vectors (32 KiB) per workgroup: many small workgroups keep
+    // more of the chip streaming than fewer large ones (measured 74 % of HBM
+    // against 66 % with 8192).
+    uint32_t rows = 2048u / R;
     if (rows < 1) rows = 1;
     const uint32_t blocks = (uint32_t)((N + rows - 1) / rows);
     if (blocks == 0) return hipSuccess;
