@@ -2,7 +2,7 @@
 //
 // For KV head kh the g = hq/hkv query heads sharing it are handled as
 // "virtual rows" v = t*g + (h - kh*g).  When g does not divide 32, the
-// dK/dV kernel's 32-row tiles do not start at token boundaries, so this pass
+// dK/dV kernel's row blocks do not start at token boundaries, so this pass
 // copies each KV head's rows into a contiguous [n_kv][rows_pad][D] buffer
 // (zero rows past N*g) that it streams with a constant stride.  One 16-byte
 // vector per thread; HBM-bound.

@@ -57,7 +57,8 @@ size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, Attn
 
 // The dK/dV kernel reads query rows of one KV head straight from q and dO
 // when its g = hq/hkv query heads per token are a power of two dividing 32
-// (then every 32-row tile starts at a token boundary); otherwise they are
+// (then every block of 32 rows, and so every tile, starts at a token
+// boundary); otherwise they are
 // gathered into the workspace first.
 inline bool attn_rows_direct(int hq, int hkv) { return 32 % (hq / hkv) == 0; }
 
