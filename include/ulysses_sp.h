@@ -122,7 +122,9 @@ sp_status ulysses_head_to_seq(const void *x_head, void *x_seq, int sp_size, int6
  *   [(q*n_kv_heads)/sp_size, ... + hl).  Elements are 16-bit and moved
  *   verbatim.  head_dim must be a multiple of 8 (SP_E_SHAPE); n_kv_heads and
  *   sp_size must divide one another and n_tokens % sp_size == 0
- *   (SP_E_NOT_DIVISIBLE); pointers 16-byte aligned.
+ *   (SP_E_NOT_DIVISIBLE); pointers 16-byte aligned.  SP_E_SHAPE also when
+ *   n_tokens * n_kv_heads * head_dim / 8 reaches 2^31 or sp_size * n_groups
+ *   exceeds 65535.
  */
 sp_status ulysses_seq_to_head_kv(const void *x_seq, void *x_head, int sp_size, int64_t n_tokens,
                                  int n_groups, int n_kv_heads, int head_dim, int rank,

@@ -224,6 +224,10 @@ def test_kv_relayout_validation(fn):
     assert fn(N=0) == _lib.SP_OK
     assert fn(src=MIS, dst=A16) == _lib.SP_E_ALIGN
     assert fn(src=A16, dst=None) == _lib.SP_E_NULL
+    # the copy indexes tokens x KV heads x 16-byte chunks in 31 bits
+    assert fn(P=16, N=2**27, G=1, H=2, d=64) == _lib.SP_E_SHAPE       # 2^27 * 2 * 8 = 2^31
+    assert fn(P=16, N=2**27 - 16, G=1, H=2, d=64) == _lib.SP_E_NULL
+    assert fn(P=256, N=256, G=256, H=1, d=8) == _lib.SP_E_SHAPE       # sp_size * groups > 65535
 
 
 def test_kv_grad_dtype():

@@ -39,7 +39,8 @@ sp_status check_kv_relayout(const void *src, const void *dst, int P, int64_t N, 
     if (rank < -1 || rank >= P) return SP_E_RANK;
     if (d % 8 != 0) return SP_E_SHAPE;
     const int64_t hl = H >= P ? H / P : 1;
-    if (N * hl * (d / 8) >= ((int64_t)1 << 31) || (N / P) * G * H * (d / 8) >= ((int64_t)1 << 31) ||
+    if (N * hl * (d / 8) >= ((int64_t)1 << 31) || N * H * (d / 8) >= ((int64_t)1 << 31) ||
+        (N / P) * G * H * (d / 8) >= ((int64_t)1 << 31) ||
         (int64_t)P * G > 65535)
         return SP_E_SHAPE;
     if (N == 0) return SP_OK;

@@ -14,8 +14,9 @@
 //   x_seq  [P][N/P][G][n_kv][d]  (token n = p N/P + t)
 //   x_head [P][G][N][hl][d], hl = max(n_kv / P, 1); rank q holds KV heads
 //          [(q n_kv)/P, (q n_kv)/P + hl)
-// One thread moves one 16-byte chunk (8 bf16).  The gradient sum runs in
-// fp32 in ascending rank order and is rounded once to the output type.
+// One thread moves one 16-byte chunk (8 bf16); the copy reads each chunk
+// once and writes it to every rank that holds its head.  The gradient sum
+// runs in fp32 in ascending rank order and is rounded once to the output type.
 #include "common.h"
 #include "launch.h"
 
@@ -23,21 +24,32 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// dst rank block y = qi * G + g (qi indexes the ranks produced);
-// x = chunk over [n][i][c] of that block.
+// grid.y = group g; x = chunk over [n][j][c] of the heads read (all H heads
+// for every rank, or the hl heads of one rank).  Each chunk is read once and
+// written to every rank that holds its head: the one owner when n_kv >= P,
+// else the R = P / n_kv consecutive ranks [j R, (j+1) R).
 __global__ __launch_bounds__(kThreads) void k_kv_seq_to_head(
     const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, int N, int G, int H, int P, int hl,
-    int V, FastDiv f_row, int q_first, int64_t chunks) {
+    int V, FastDiv f_row, int rank, int64_t chunks) {
     const int64_t x = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (x >= chunks) return;
-    const int qi = blockIdx.y / G, g = blockIdx.y - (blockIdx.y / G) * G;
-    const int q = q_first + qi;
-    const uint32_t row_chunks = (uint32_t)(hl * V);
+    const int g = blockIdx.y;
     const uint32_t n = fdiv((uint32_t)x, f_row);
-    const uint32_t cc = (uint32_t)x - n * row_chunks;            // i * V + c
-    const int h0 = (int)(((int64_t)q * H) / P);
-    const u32x4 val = src[((int64_t)n * G + g) * H * V + (int64_t)h0 * V + cc];
-    dst[(((int64_t)qi * G + g) * N + n) * row_chunks + cc] = val;
+    const uint32_t jc = (uint32_t)x - n * f_row.d;                 // head * V + c, heads read
+    const uint32_t jl = jc / (uint32_t)V, c = jc - jl * (uint32_t)V;
+    const int h0 = rank < 0 ? 0 : (int)(((int64_t)rank * H) / P);
+    const int j = h0 + (int)jl;                                      // KV head
+    const u32x4 val = __builtin_nontemporal_load(src + ((int64_t)n * G + g) * H * V + (int64_t)j * V + c);
+    if (rank >= 0) {
+        __builtin_nontemporal_store(val, dst + (((int64_t)g * N + n) * hl + jl) * V + c);
+    } else if (H >= P) {
+        const int q = j / hl, i = j - q * hl;
+        __builtin_nontemporal_store(val, dst + ((((int64_t)q * G + g) * N + n) * hl + i) * V + c);
+    } else {
+        const int R = P / H;
+        for (int r = 0; r < R; ++r)
+            __builtin_nontemporal_store(val, dst + (((int64_t)(j * R + r) * G + g) * N + n) * V + c);
+    }
 }
 
 // dst rank block y = pi (token chunk of rank p_first + pi);
@@ -106,13 +118,13 @@ hipError_t launch_kv_seq_to_head(const void *x_seq, void *x_head, int P, int64_t
                                  int d, int rank, hipStream_t stream) {
     const int hl = H >= P ? H / P : 1;
     const int V = d / 8;
-    const int64_t chunks = N * hl * V;
-    const int nq = rank < 0 ? P : 1;
-    const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads), (unsigned)(nq * G));
+    const int heads_read = rank < 0 ? H : hl;
+    const int64_t chunks = N * heads_read * V;
+    const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads), (unsigned)G);
     KernelTimer timer("relayout_kv_seq_to_head", stream);
     hipLaunchKernelGGL(k_kv_seq_to_head, grid, dim3(kThreads), 0, stream, (const u32x4 *)x_seq,
-                       (u32x4 *)x_head, (int)N, G, H, P, hl, V, make_fastdiv((uint32_t)(hl * V)),
-                       rank < 0 ? 0 : rank, chunks);
+                       (u32x4 *)x_head, (int)N, G, H, P, hl, V,
+                       make_fastdiv((uint32_t)(heads_read * V)), rank, chunks);
     return hipGetLastError();
 }
 
