@@ -1,0 +1,111 @@
+"""Host logic of bench.py, on the CPU: the HBM-traffic summary built from rocprofv3 counter
+files (calibration against the plain copy, kernel-name matching, per-dispatch averages),
+the source-hash guard on the committed summary, the kernel-trace table, and the refusal
+to run on more than one GPU."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _counter_csv(path, counter, rows):
+    """rows: (dispatch_id, kernel_name, values per counter instance)."""
+    with open(path, "w") as fh:
+        fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for did, name, vals in rows:
+            for v in vals:
+                fh.write(f'{did},"{name}",{counter},{v}\n')
+
+
+def test_traffic_summary_calibrates_against_the_copy(tmp_path):
+    from synth import configs
+    w = configs.WORKLOADS[4]
+    copy_bytes = 2 * w.n_tokens * w.relayout_groups * w.relayout_heads * w.head_dim
+    # FETCH_SIZE reads half the copied bytes, WRITE_SIZE all of them (split over 2 instances)
+    f_copy = copy_bytes / 2 / 1024
+    w_copy = copy_bytes / 1024
+    dkdv = "void (anonymous namespace)::k_attn_bwd_dkdv<128>(bf16 const*, ...)"
+    mangled_fwd = "_ZN12_GLOBAL__N_110k_attn_fwdILi128EEEvPKDF16bS2_"
+    decoy = "k_attn_bwd_dkdv_helper(int)"          # must not count as the dK/dV kernel
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [
+        (1, "__amd_rocclr_copyBuffer", [f_copy / 2, f_copy / 2]),
+        (2, dkdv, [100.0, 200.0]),                 # 300 KiB
+        (3, dkdv, [250.0, 250.0]),                 # 500 KiB -> average 400
+        (4, mangled_fwd, [64.0]),
+        (5, decoy, [1e9]),
+    ])
+    _counter_csv(write, "WRITE_SIZE", [
+        (1, "__amd_rocclr_copyBuffer", [w_copy]),
+        (2, dkdv, [10.0]),
+        (3, dkdv, [30.0]),                         # average 20
+        (4, mangled_fwd, [8.0]),
+        (5, decoy, [1e9]),
+    ])
+    text = bench.summarize_traffic(str(fetch), str(write))
+    assert "FETCH_SIZE: copy reads" in text and "factor 2.0000" in text
+    assert "WRITE_SIZE: copy reads" in text and "factor 1.0000" in text
+    lines = {ln.split()[0]: dict(t.split("=", 1) for t in ln.split())
+             for ln in text.splitlines() if ln.startswith("kernel=")}
+    d = lines["kernel=attn_bwd_dkdv"]
+    assert d["dispatches"] == "2"
+    assert float(d["traffic_bytes"]) == pytest.approx(400 * 1024 * 2 + 20 * 1024)
+    assert d["sources"] == bench.sources_hash("attn_bwd_dkdv")
+    f = lines["kernel=attn_fwd"]
+    assert float(f["traffic_bytes"]) == pytest.approx(64 * 1024 * 2 + 8 * 1024)
+    assert "kernel=attn_bwd_dq" not in lines
+
+
+def test_traffic_summary_needs_a_copy(tmp_path):
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [(1, "k_attn_fwd<128>(x)", [1.0])])
+    _counter_csv(write, "WRITE_SIZE", [(1, "k_attn_fwd<128>(x)", [1.0])])
+    with pytest.raises(SystemExit):
+        bench.summarize_traffic(str(fetch), str(write))
+
+
+def test_load_traffic_checks_the_source_hash(tmp_path, monkeypatch):
+    good = bench.sources_hash("attn_bwd_dkdv")
+    path = tmp_path / "traffic.txt"
+    path.write_text("# header\n"
+                    f"kernel=attn_bwd_dkdv dispatches=3 fetch_kib=1 write_kib=1 traffic_bytes=12345 sources={good}\n"
+                    "kernel=attn_fwd dispatches=3 fetch_kib=1 write_kib=1 traffic_bytes=999 sources=0000000000000000\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    assert bench.load_traffic("attn_bwd_dkdv") == 12345.0
+    assert bench.load_traffic("attn_fwd") is None          # taken from other sources
+    assert bench.load_traffic("attn_bwd_dq") is None       # absent
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
+    assert bench.load_traffic("attn_bwd_dkdv") is None
+
+
+def test_source_hash_ignores_comments_only():
+    h = bench.sources_hash("attn_bwd_dkdv")
+    assert h == bench.sources_hash("attn_bwd_dq")          # same source file
+    assert h != bench.sources_hash("attn_fwd")
+    assert len(h) == 16
+
+
+def test_trace_summary_table(tmp_path):
+    p = tmp_path / "stats.csv"
+    p.write_text("Name,Calls,TotalDurationNs,AverageNs,Percentage\n"
+                 '"void k_attn_fwd<128>(...)",3,300000,100000,75.0\n'
+                 '"k_loss_rank(...)",3,100000,33333.3,25.0\n')
+    text = bench.summarize_trace(str(p)).splitlines()
+    assert text[0].split() == ["kernel", "calls", "total_us", "avg_us", "pct"]
+    assert text[1].split()[-4:] == ["3", "300.0", "100.0", "75.00%"]
+    assert len(text) == 3
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
