@@ -124,15 +124,16 @@ def test_workspace_bytes():
     assert f(0, 4, 1, 128) == 0 or f(0, 4, 1, 128) < 4096
     small, big = f(1000, 8, 2, 128), f(2000, 8, 2, 128)
     assert 0 < small < big
-    # at least the per-token segment bounds and the per-row statistics; when
-    # the query heads per KV head do not divide 32, also the virtual-row
-    # copies of Q and dO
+    # at least the per-token segment bounds, the per-row statistics and the
+    # forward's transposed copy of V (2 * hkv * d bytes per token); when the
+    # query heads per KV head do not divide 32, also the virtual-row copies of
+    # Q and dO
     N, d = 524288, 128
-    base = lambda hq: 8 * N + 8 * hq * N
-    assert base(4) <= f(N, 4, 1, d) < base(4) + (1 << 20)
-    assert base(8) <= f(N, 8, 2, d) < base(8) + (1 << 20)          # g = 4: read in place
+    base = lambda hq, hkv: 8 * N + 8 * hq * N + 2 * hkv * d * N
+    assert base(4, 1) <= f(N, 4, 1, d) < base(4, 1) + (1 << 20)
+    assert base(8, 2) <= f(N, 8, 2, d) < base(8, 2) + (1 << 20)       # g = 4: read in place
     copies = 2 * 2 * 6 * d * N
-    assert base(6) + copies <= f(N, 6, 2, d) < base(6) + copies + (1 << 20)   # g = 3
+    assert base(6, 2) + copies <= f(N, 6, 2, d) < base(6, 2) + copies + (1 << 20)   # g = 3
 
 
 def _loss(**kw):

@@ -88,6 +88,7 @@ size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, Attn
     w.qv = gather ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
     w.dov = gather ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
     w.rowstat = (float *)take(8 * (size_t)hkv * Mpad);
+    w.vt = take(2 * (size_t)hkv * d * pad64(N));
     if (ws) *ws = w;
     return off;
 }

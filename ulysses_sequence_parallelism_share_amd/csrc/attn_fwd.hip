@@ -17,15 +17,16 @@
 //    query column: the row max and row sum of the softmax are per-lane
 //    register reductions plus one exchange with lane l^32.
 //  * The probabilities leave the S^T accumulators directly as the B operand
-//    of O^T += V^T P^T; the V^T operand is read from the natural V tile with
-//    transposing LDS reads (ds_read_b64_tr_b16) in the accumulators' key
-//    order, and the per-row rescale of O is a per-lane multiply.
+//    of O^T += V^T P^T, and the per-row rescale of O is a per-lane multiply.
+//    The V^T operand comes from V^T tiles ([d][keys], 16-byte reads like the
+//    K tiles) of a transposed copy of V that a pre-pass writes with the keys
+//    of every group of 16 in the accumulators' order: lane half h holds keys
+//    4h..4h+3 and 8+4h..8+4h+3 of each group in its 8 k-slots.
 //  * fp32 online softmax in the log2 domain (scale * log2(e) folded into one
 //    FMA per score, exponentials with v_exp_f32); the running max is
 //    updated lazily (only when it grows by more than 2^8), so the O
 //    accumulators are rarely rescaled.
-//  * One workgroup per CU (2 waves per SIMD): one wave's softmax overlaps
-//    the other's MFMAs.
+//  * One workgroup of 8 waves per CU (2 waves per SIMD).
 //  * K and V tiles are double-buffered in LDS (XOR-swizzled, bank-conflict
 //    free) and filled by direct global->LDS loads issued one tile ahead, so
 //    the loads overlap the MFMA and softmax work of the current tile without
@@ -48,16 +49,58 @@ constexpr int kWaves = kThreads / 64;
 
 template <int D>
 struct FwdSmem {
-    using K = SwzTile<BN, D / 8>;   // keys x features (K and V tiles alike)
-    static constexpr int kStage = 2 * K::kBytes;
+    using K = SwzTile<BN, D / 8>;   // keys x features
+    using VT = SwzTile<D, BN / 8>;  // features x keys (permuted within groups of 16)
+    static constexpr int kStage = K::kBytes + VT::kBytes;
 };
+
+// Position p (0..15) of a group of 16 keys in the transposed copy holds key
+// kperm(p): lane half h of an MFMA operand reads positions 8h..8h+7, which
+// must be the keys its accumulator registers hold (rows 4h+{0..3} and
+// 8+4h+{0..3} of each 16-row group).
+__device__ __forceinline__ int kperm(int p) { return (p & 3) + ((p >> 2) & 1) * 8 + (p >> 3) * 4; }
+
+// V [N][hkv][d] (token stride kv_st) -> vt [hkv][d][Npad], keys permuted
+// within groups of 16, zero past N.  A workgroup transposes 64 keys of one
+// KV head through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void k_v_transpose(const bf16 *__restrict__ v, bf16 *__restrict__ vt,
+                                                     int N, int64_t Npad, int64_t kv_st) {
+    __shared__ bf16 tile[64][D + 8];   // +8: rows 16 bytes apart in bank order
+    const int kh = blockIdx.y, j0 = blockIdx.x * 64;
+    constexpr int CPR = D / 8;         // 16-byte chunks per key row
+#pragma unroll
+    for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+        const int r = i / CPR, c = i % CPR;
+        bf16x8 x;
+        if (j0 + r < N) {
+            x = *(const bf16x8 *)(v + (size_t)(j0 + r) * kv_st + (size_t)kh * D + c * 8);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (bf16)0.f;
+        }
+        *(bf16x8 *)&tile[r][c * 8] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = threadIdx.x; i < D * 8; i += 256) {   // output chunk: feature f, keys 8c..8c+7
+        const int f = i / 8, c = i % 8;
+        bf16x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int p = 8 * c + e;
+            x[e] = tile[(p & ~15) + kperm(p & 15)][f];
+        }
+        *(bf16x8 *)(vt + ((size_t)kh * D + f) * Npad + j0 + 8 * c) = x;
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(
-    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
-    const int32_t *__restrict__ kstart, bf16 *__restrict__ o, float *__restrict__ lse, int N,
-    int hq, int hkv, int g, FastDiv fg, float scale_log2, int n_row_tiles, int64_t q_st,
-    int64_t kv_st, int64_t o_st) {
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ vt,
+    int64_t vt_n, const int32_t *__restrict__ kstart, bf16 *__restrict__ o,
+    float *__restrict__ lse, int N, int hq, int hkv, int g, FastDiv fg, float scale_log2,
+    int n_row_tiles, int64_t q_st, int64_t kv_st, int64_t o_st) {
     using S = FwdSmem<D>;
     __shared__ __attribute__((aligned(1024))) char smem[2 * S::kStage];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -82,12 +125,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(
     // Keys past the end are read from the last key: finite values, always masked.
     RowStager<BN, D / 8, kWaves> stager;
     stager.init(wave, lane, (uint32_t)(kv_st * 2), 0, 0);
+    RowStager<D, BN / 8, kWaves> stager_vt;   // D feature rows of the V^T tile
+    stager_vt.init(wave, lane, (uint32_t)(vt_n * 2), 0, 0);
+    const bf16 *vt_head = vt + (size_t)kh * D * vt_n;
     auto stage = [&](int jt, int buf) {
         char *base = smem + buf * S::kStage;
         const int j0 = jt * BN;
         const size_t roff = (size_t)j0 * kv_st + kh * D;
         stager.issue(base, wave, lane, k + roff, N - j0);
-        stager.issue(base + S::K::kBytes, wave, lane, v + roff, N - j0);
+        stager_vt.issue(base + S::K::kBytes, wave, lane, vt_head + j0, D);
     };
     stage(jt0, 0);
 
@@ -172,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const bf16x8 a = read_tr8<typename S::K>(vs, kb * 32 + 16 * s2, db * 32, lane);
+                    const bf16x8 a = *(const bf16x8 *)(vs + S::VT::off(db * 32 + col, kb * 4 + 2 * s2 + half));
                     oacc[db] = mfma32(a, pf[kb][s2], oacc[db]);
                 }
     };
@@ -217,15 +263,29 @@ hipError_t launch_attn_fwd(const void *q, const void *k, const void *v, const in
     const int n_row_tiles = (M + BM - 1) / BM;
     const FastDiv fg = make_fastdiv((uint32_t)g);
     const float scale_log2 = scale * SP_LOG2E;
+    const int64_t n_pad = (N + BN - 1) / BN * BN;
+    {
+        const dim3 tgrid((unsigned)(n_pad / 64), (unsigned)hkv);
+        KernelTimer timer("attn_fwd_v_transpose", stream);
+        if (d == 128)
+            hipLaunchKernelGGL(k_v_transpose<128>, tgrid, dim3(256), 0, stream, (const bf16 *)v,
+                               (bf16 *)ws.vt, (int)N, n_pad, st.k);
+        else
+            hipLaunchKernelGGL(k_v_transpose<64>, tgrid, dim3(256), 0, stream, (const bf16 *)v,
+                               (bf16 *)ws.vt, (int)N, n_pad, st.k);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     const dim3 grid((unsigned)(n_row_tiles * hkv));
     KernelTimer timer("attn_fwd", stream);
     if (d == 128)
         hipLaunchKernelGGL(k_attn_fwd<128>, grid, dim3(kThreads), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, (const bf16 *)v, ws.kstart, (bf16 *)o, lse,
-                           (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles, st.q, st.k, st.o);
+                           (const bf16 *)k, (const bf16 *)ws.vt, n_pad, ws.kstart, (bf16 *)o,
+                           lse, (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles, st.q, st.k,
+                           st.o);
     else
         hipLaunchKernelGGL(k_attn_fwd<64>, grid, dim3(kThreads), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, (const bf16 *)v, ws.kstart, (bf16 *)o, lse,
-                           (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles, st.q, st.k, st.o);
+                           (const bf16 *)k, (const bf16 *)ws.vt, n_pad, ws.kstart, (bf16 *)o,
+                           lse, (int)N, hq, hkv, g, fg, scale_log2, n_row_tiles, st.q, st.k,
+                           st.o);
     return hipGetLastError();
 }

@@ -51,6 +51,7 @@ struct AttnWorkspace {
     void *qv;          // bwd, groups not dividing 32: Q in virtual-row order  [hkv][Mpad][d]
     void *dov;         // bwd, groups not dividing 32: dO in virtual-row order [hkv][Mpad][d]
     float *rowstat;    // bwd: lse*log2e and rowsum(dO*O) per 32-row block [hkv][Mpad/32][2][32]
+    void *vt;          // fwd: V transposed, keys permuted within groups of 16 [hkv][d][Npad]
 };
 
 size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws);
