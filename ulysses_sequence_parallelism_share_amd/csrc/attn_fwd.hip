@@ -27,7 +27,7 @@
 //    updated lazily (only when it grows by more than 2^8), so the O
 //    accumulators are rarely rescaled.
 //  * One workgroup of 8 waves per CU (2 waves per SIMD).
-//  * K and V tiles are double-buffered in LDS (XOR-swizzled, bank-conflict
+//  * K and V^T tiles are double-buffered in LDS (XOR-swizzled, bank-conflict
 //    free) and filled by direct global->LDS loads issued one tile ahead, so
 //    the loads overlap the MFMA and softmax work of the current tile without
 //    occupying registers.
