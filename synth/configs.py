@@ -142,6 +142,8 @@ LCE_WORKLOADS = {
     11: LceWorkload(11, "lce-small-n300-v1000-k256", 300, 256, 1000),
     12: LceWorkload(12, "lce-llama2-vocab-n1024-v32000-k1024", 1024, 1024, 32000),
     13: LceWorkload(13, "lce-llama3-8b-lmhead-n4096-v128256-k4096", 4096, 4096, 128256),
+    14: LceWorkload(14, "lce-odd-vocab-n130-v997-k256", 130, 256, 997),
+    15: LceWorkload(15, "lce-tiny-vocab-n70-v3-k512", 70, 512, 3),
 }
 
 

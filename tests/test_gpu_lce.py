@@ -52,6 +52,16 @@ def test_lce_small_chunked_parity():
     _check_full(inp, _run(inp, 128))
 
 
+@pytest.mark.parametrize("cfg", [14, 15])
+def test_lce_vocab_not_a_multiple_of_four(cfg):
+    """Vocabularies of 997 and 3 entries: the row pass reads the logits in 16-byte
+    pieces, so the last piece of every row is partly past the vocabulary."""
+    w = configs.LCE_WORKLOADS[cfg]
+    say(f"lce {w.name}")
+    inp = configs.lce_inputs(w)
+    _check_full(inp, _run(inp, 64))
+
+
 def test_lce_chunking_forward_only_and_bad_labels():
     """Chunk size changes only the order of dw's sum over chunks: losses, lse and dx
     are bit-identical, dw within rounding; the forward-only call gives the same bits;
