@@ -443,8 +443,8 @@ def main():
     dkdv_ms = kt["attn_bwd_dkdv"]["avg_ms"]
     dq_ms = kt["attn_bwd_dq"]["avg_ms"]
     attn_kernel_ms = sum(per_step.get(n, 0.0) for n in
-                         ("segment_chunks", "segment_scan", "gather_rows", "attn_fwd",
-                          "bwd_rowstats", "attn_bwd_dkdv", "attn_bwd_dq"))
+                         ("segment_chunks", "segment_scan", "gather_rows", "attn_fwd_v_transpose",
+                          "attn_fwd", "bwd_rowstats", "attn_bwd_dkdv", "attn_bwd_dq"))
     algo = {"attn_fwd": fwd_flop, "attn_bwd_dkdv": 0.8 * bwd_flop, "attn_bwd_dq": 0.2 * bwd_flop}
     dom = max(algo, key=lambda n: kt[n]["avg_ms"])
     dom_tflops = algo[dom] / kt[dom]["avg_ms"] / 1e9
