@@ -195,10 +195,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkdv(
         stager_q.issue(base + S::kQ, wave, lane, q_head + tok0 * rs.q_tok_bytes, rs.rows - vq0);
         stager_do.issue(base + S::kDO, wave, lane, do_head + tok0 * rs.do_tok_bytes, rs.rows - vq0);
         if (lane < S::kStatLanes)   // every wave: its 16-byte pieces of the rows' statistics
-            __builtin_amdgcn_global_load_lds(
-                (const void *)((const char *)(rowstat + ((size_t)kh * Mpad + vq0) * 2) +
-                               (wave * S::kStatLanes + lane) * 16),
-                (lds_byte *)(base + S::kStat + wave * S::kStatLanes * 16), 16, 0, 0);
+            dma16((const void *)((const char *)(rowstat + ((size_t)kh * Mpad + vq0) * 2) +
+                                 (wave * S::kStatLanes + lane) * 16),
+                  (lds_byte *)(base + S::kStat + wave * S::kStatLanes * 16));
     };
     for (int i = 0; i < kDkdvAhead && i < n_it; ++i) stage(i, i);
 

@@ -54,6 +54,19 @@ struct SwzTile {
 // then costs one address add per load.  In a tile with fewer than ROWS valid
 // rows (the last one), rows at or past `valid_rows` are read from row
 // valid_rows - 1 instead (the caller makes such rows harmless).
+// One direct global->LDS load of 16 bytes per lane (lane i to lds + 16 i:
+// the LDS base goes in M0), issued through inline assembly.  The compiler's
+// own form makes every later transposing LDS read wait for all direct loads
+// in flight (it cannot tell that they write other bytes), which drains the
+// prefetch of the next tile; here the callers' s_waitcnt vmcnt and
+// workgroup barrier alone publish the data (the compiler's waits for its
+// own loads stay correct: loads complete in issue order).
+__device__ __forceinline__ void dma16(const void *g, lds_byte *l) {
+    const uint32_t la = (uint32_t)(uintptr_t)l;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(la) : "memory", "m0");
+}
+
 template <int ROWS, int CH, int NWAVES>
 struct RowStager {
     using T = SwzTile<ROWS, CH>;
@@ -86,8 +99,7 @@ struct RowStager {
 #pragma unroll
             for (int k = 0; k < kPer; ++k)
                 if (mine(wave, k))
-                    __builtin_amdgcn_global_load_lds((const void *)(src + off[k]),
-                                                     lds + (wave + k * NWAVES) * 1024, 16, 0, 0);
+                    dma16((const void *)(src + off[k]), lds + (wave + k * NWAVES) * 1024);
             return;
         }
         for (int k = 0; k < kPer; ++k) {
@@ -96,8 +108,7 @@ struct RowStager {
             const int rs = i * (64 / CH) + lane / CH;          // LDS row of this slot
             const int r = rs < valid_rows ? rs : valid_rows - 1; // source row it holds
             const int c = (lane & (CH - 1)) ^ T::swz(rs);
-            __builtin_amdgcn_global_load_lds((const void *)(src + row_off(r) + c * 16),
-                                             lds + i * 1024, 16, 0, 0);
+            dma16((const void *)(src + row_off(r) + c * 16), lds + i * 1024);
         }
     }
 };
