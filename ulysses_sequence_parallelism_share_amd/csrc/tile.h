@@ -60,11 +60,12 @@ struct SwzTile {
 // in flight (it cannot tell that they write other bytes), which drains the
 // prefetch of the next tile; here the callers' s_waitcnt vmcnt and
 // workgroup barrier alone publish the data (the compiler's waits for its
-// own loads stay correct: loads complete in issue order).
+// own loads stay correct: loads complete in issue order).  M0 is an input
+// operand, so the compiler writes it and knows its value; the s_nop is the
+// wait state between that write and the load reading M0.
 __device__ __forceinline__ void dma16(const void *g, lds_byte *l) {
     const uint32_t la = (uint32_t)(uintptr_t)l;
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(la) : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "{m0}"(la) : "memory");
 }
 
 template <int ROWS, int CH, int NWAVES>
