@@ -29,13 +29,23 @@ CFLAGS = [
 ]
 
 
+# Machine-scheduler strategy per source (LLVM AMDGPU option), measured on the
+# 500K-token rank share against the default strategy in alternating runs:
+# the forward 2.4 % faster with iterative-ilp, the dK/dV kernel 1.3 % faster
+# with max-ilp (dQ unchanged); other sources keep the default.
+PER_SOURCE_FLAGS = {
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *PER_SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
