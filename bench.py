@@ -49,6 +49,9 @@ def parse():
                     help="timed calls of the fused cross-entropy workload (0: skip)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="print a text summary of a rocprofv3 --stats kernel table and exit")
+    ap.add_argument("--summarize-counters", metavar="COUNTER_CSV",
+                    help="print the MFMA/LDS counter summary of one rocprofv3 --pmc run of "
+                         "COUNTER_PASS and exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM-traffic summary of two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, then WRITE_SIZE) and exit")
@@ -200,6 +203,61 @@ def load_traffic(kernel):
     return None
 
 
+COUNTER_PASS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES "
+                "GRBM_GUI_ACTIVE SQ_INSTS_LDS SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT")
+N_XCD, N_SIMD = 8, 1024        # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def summarize_counters(csv_path):
+    """MFMA and LDS figures of the attention kernels from one rocprofv3 --pmc run of
+    COUNTER_PASS: bf16 MFMA FLOP (MOPS x 512) against the kernel's executed FLOP, the
+    clock the kernel ran at (GRBM_GUI_ACTIVE is summed over the 8 XCDs), MFMA busy
+    cycles per SIMD-cycle (the profiler's MfmaUtil) and LDS bank conflicts."""
+    import csv
+    from synth import configs
+    w = configs.WORKLOADS[5]
+    A, hq, d = w.allowed_pairs(), w.hq, w.head_dim
+    executed = {"attn_fwd": 4 * d * A * hq, "attn_bwd_dkdv": 8 * d * A * hq,
+                "attn_bwd_dq": 6 * d * A * hq}
+    disp = {}
+    with open(csv_path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            e = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": {},
+                                                         "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = ["# MFMA and LDS counters per dispatch, 500K-token rank share (N=524288, hq=4, hkv=1,",
+           "# d=128, 4 packed samples)",
+           "# commands (GPU, from /tmp with TMPDIR=/tmp; REPO = the repository root):",
+           f"#   rocprofv3 --pmc {COUNTER_PASS} --output-format csv -d REPO/gpurun_out/pmc_sq -o run "
+           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0 --lce-steps 1",
+           "#   python3 REPO/bench.py --summarize-counters REPO/gpurun_out/pmc_sq/run_counter_collection.csv",
+           "# mfma_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (executed_flop: 4/8/6 d A hq for fwd/dK,dV/dQ);",
+           "# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+           "# (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), the share of SIMD-cycles with the matrix unit busy at",
+           "# the clock the kernel ran at; tflops_at_clock_peak = 1024 FLOP x 1024 SIMDs x clock;",
+           "# lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. Averages over the dispatches."]
+    for kernel, sym in KERNEL_SYMBOL.items():
+        pat = re.compile(r"(^|[\s:\d])" + sym + r"([<(]|I[LZN])")
+        rows = [e for e in disp.values() if pat.search(e["name"])]
+        if not rows:
+            continue
+        n = len(rows)
+        avg = lambda f: sum(f(e) for e in rows) / n
+        ms = avg(lambda e: e["ns"]) / 1e6
+        gui = avg(lambda e: e["c"]["GRBM_GUI_ACTIVE"]) / N_XCD
+        flop = avg(lambda e: e["c"]["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512
+        busy = avg(lambda e: e["c"]["SQ_VALU_MFMA_BUSY_CYCLES"]) / (gui * N_SIMD)
+        clk = gui / (ms * 1e-3) / 1e9
+        idx = avg(lambda e: e["c"]["SQ_LDS_IDX_ACTIVE"])
+        conf = avg(lambda e: e["c"]["SQ_LDS_BANK_CONFLICT"]) / idx if idx else 0.0
+        out.append(f"kernel={kernel} dispatches={n} avg_ms={ms:.2f} clock_ghz={clk:.3f} "
+                   f"mfma_flop={flop:.4e} executed_flop={executed[kernel]:.4e} "
+                   f"tflops={flop / ms / 1e9:.1f} tflops_at_clock_peak={1024 * N_SIMD * clk / 1e3:.1f} "
+                   f"mfma_busy={busy:.3f} lds_insts={avg(lambda e: e['c']['SQ_INSTS_LDS']):.4e} "
+                   f"lds_conflict={conf:.4f}")
+    return "\n".join(out)
+
+
 def summarize_trace(stats_csv):
     import csv
     rows = []
@@ -341,6 +399,9 @@ def main():
         return
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

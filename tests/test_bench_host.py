@@ -62,6 +62,45 @@ def test_traffic_summary_calibrates_against_the_copy(tmp_path):
     assert "kernel=attn_bwd_dq" not in lines
 
 
+def test_counter_summary_formulas(tmp_path):
+    """MFMA FLOP = MOPS x 512; the clock and the busy share use GRBM_GUI_ACTIVE per XCD
+    (the profiler sums it over the 8 XCDs); several counter instances of one dispatch are
+    summed; dispatches are averaged; other kernels are ignored."""
+    from synth import configs
+    w = configs.WORKLOADS[5]
+    fwd = "void (anonymous namespace)::k_attn_fwd<128>(bf16 const*, ...)"
+    path = tmp_path / "sq.csv"
+    ms = 2.0                                            # 2 ms per dispatch
+    gui_per_xcd = 3.6e6                                 # 1.8 GHz over 2 ms
+    busy = 0.5 * gui_per_xcd * 1024                     # half of the SIMD-cycles
+    with open(path, "w") as fh:
+        fh.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n")
+        for did in (7, 9):
+            rows = [("GRBM_GUI_ACTIVE", [gui_per_xcd] * 8),
+                    ("SQ_INSTS_VALU_MFMA_MOPS_BF16", [1e9, 1e9]),
+                    ("SQ_VALU_MFMA_BUSY_CYCLES", [busy / 4] * 4),
+                    ("SQ_INSTS_LDS", [5.0]), ("SQ_LDS_IDX_ACTIVE", [100.0]),
+                    ("SQ_LDS_BANK_CONFLICT", [10.0 if did == 7 else 30.0])]
+            for name, vals in rows:
+                for v in vals:
+                    fh.write(f'{did},"{fwd}",{name},{v},1000,{1000 + int(ms * 1e6)}\n')
+        fh.write('8,"k_relayout<true>(...)",SQ_INSTS_LDS,1e12,0,1\n')
+    text = bench.summarize_counters(str(path))
+    lines = {ln.split()[0]: dict(t.split("=", 1) for t in ln.split())
+             for ln in text.splitlines() if ln.startswith("kernel=")}
+    assert list(lines) == ["kernel=attn_fwd"]
+    f = lines["kernel=attn_fwd"]
+    assert f["dispatches"] == "2"
+    assert float(f["avg_ms"]) == pytest.approx(ms)
+    assert float(f["clock_ghz"]) == pytest.approx(1.8)
+    assert float(f["mfma_flop"]) == pytest.approx(2e9 * 512, rel=1e-4)
+    assert float(f["mfma_busy"]) == pytest.approx(0.5)
+    assert float(f["tflops_at_clock_peak"]) == pytest.approx(1024 * 1024 * 1.8 / 1e3, rel=1e-3)
+    assert float(f["lds_conflict"]) == pytest.approx(0.2)
+    A = w.allowed_pairs()
+    assert float(f["executed_flop"]) == pytest.approx(4 * w.head_dim * A * w.hq, rel=1e-4)
+
+
 def test_traffic_summary_needs_a_copy(tmp_path):
     fetch = tmp_path / "fetch.csv"
     write = tmp_path / "write.csv"
