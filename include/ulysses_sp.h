@@ -179,7 +179,10 @@ size_t sp_attn_workspace_bytes(int64_t n_tokens, int n_q_heads, int n_kv_heads, 
  *   workspace     >= sp_attn_workspace_bytes(...) bytes of device memory
  * n_q_heads and n_kv_heads are the LOCAL (per-rank) head counts.
  * head_dim must be 64 or 128 (else SP_E_SHAPE); n_q_heads % n_kv_heads != 0
- * gives SP_E_NOT_DIVISIBLE.  n_tokens == 0 is a no-op.
+ * gives SP_E_NOT_DIVISIBLE.  Size limits (else SP_E_SHAPE): n_tokens *
+ * n_q_heads < 2^30, and head_dim * (n_tokens rounded up to 64) * 2 <= 2^32,
+ * i.e. at most 16,777,216 tokens at head_dim 128 (33,554,432 at 64); the
+ * same limits apply to sp_attn_bwd.  n_tokens == 0 is a no-op.
  * Arithmetic: bf16 MFMA products with fp32 accumulation and an fp32 online
  * softmax; probabilities are rounded to bf16 before the product with V.
  */

@@ -102,6 +102,8 @@ def test_attention_validation():
         assert fn(scale=float("nan")) == _lib.SP_E_SHAPE
         assert fn(scale=float("inf")) == _lib.SP_E_SHAPE
         assert fn(N=1 << 29, hq=4) == _lib.SP_E_SHAPE      # virtual rows exceed the index range
+        assert fn(N=(1 << 24) + 1, hq=1) == _lib.SP_E_SHAPE  # V^T tile offsets exceed 32 bits
+        assert fn(N=(1 << 24) + 1, hq=1, d=64) != _lib.SP_E_SHAPE
         assert fn(N=0) == _lib.SP_OK
         p = dict(ptrs)
         p["q"] = MIS

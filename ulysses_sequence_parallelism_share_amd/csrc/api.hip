@@ -54,6 +54,10 @@ sp_status check_attn_shape(int64_t N, int hq, int hkv, int d, float scale) {
     if (d != 64 && d != 128) return SP_E_SHAPE;
     if (hq % hkv != 0) return SP_E_NOT_DIVISIBLE;
     if (N * (int64_t)hq >= kMaxRows) return SP_E_SHAPE;
+    // Tile rows are addressed by 32-bit byte offsets from the tile base; the
+    // longest span is the forward's V^T tile: head_dim rows of the transposed
+    // copy, (n_tokens rounded up to 64) keys each.
+    if ((int64_t)d * ((N + 63) / 64 * 64) * 2 > ((int64_t)1 << 32)) return SP_E_SHAPE;
     if (!(scale >= 0.f) || isinf(scale)) return SP_E_SHAPE;
     return SP_OK;
 }

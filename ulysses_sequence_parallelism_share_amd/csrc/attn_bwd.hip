@@ -183,7 +183,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkdv(
     // do_rows (`RowSource`); tiles start at multiples of 32 rows, hence at
     // token boundaries.  Rows past the end are read from the last row: finite
     // data, and their statistics make P exactly 0.
-    RowStager<TQ, D / 8, W> stager_q, stager_do;
+    RowStager<TQ, D / 8, W, false> stager_q, stager_do;
     stager_q.init(wave, lane, rs.q_tok_bytes, D * 2, rs.gshift);
     stager_do.init(wave, lane, rs.do_tok_bytes, D * 2, rs.gshift);
     const char *q_head = (const char *)q_rows + (size_t)kh * rs.q_head_bytes;

@@ -66,8 +66,12 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16 &a, int base) {
 }
 
 __device__ __forceinline__ float wave_max_pair(float x) {
-    // lanes l and l ^ 32 hold the two halves of one column
-    return fmaxf(x, __shfl_xor(x, 32));
+    // lanes l and l ^ 32 hold the two halves of one column; v_permlane32_swap
+    // exchanges the upper half of one copy with the lower half of the other,
+    // so every lane sees both values without an LDS round trip
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
