@@ -152,13 +152,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(
         for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
     float m_run = -1e30f, l_run = 0.f;
 
-    // One key tile; `masked` selects the code that evaluates the mask.
-    auto tile_step = [&](int jt, auto masked) {
+    // One key tile; `masked` selects the code that evaluates the mask.  The
+    // LDS slot of tile jt is (jt - jt0) & 1; `slot` passes it as a constant
+    // where the caller knows it (0 or 1), or -1 to compute it.
+    auto tile_step = [&](int jt, auto masked, auto slot) {
         const int j0 = jt * BN;
         wait_async();
         __syncthreads();
-        if (jt < jt1) stage(jt + 1, (jt + 1 - jt0) & 1);
-        const char *ks = smem + ((jt - jt0) & 1) * S::kStage;
+        const int sl = decltype(slot)::value >= 0 ? decltype(slot)::value : ((jt - jt0) & 1);
+        if (jt < jt1) stage(jt + 1, sl ^ 1);
+        const char *ks = smem + sl * S::kStage;
         const char *vs = ks + S::K::kBytes;
 
         f32x16 s[2];
@@ -228,10 +231,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fwd(
     // Separate loops keep the mask code out of the unmasked tiles entirely.
     const int fa = max(jt0, (ks_max + BN - 1) / BN);
     const int fb = min(jt1, t_first >= BN - 1 ? (t_first - (BN - 1)) / BN : -1);
+    using dyn = std::integral_constant<int, -1>;
+    using s0 = std::integral_constant<int, 0>;
+    using s1 = std::integral_constant<int, 1>;
     int jt = jt0;
-    for (; jt <= jt1 && jt < fa; ++jt) tile_step(jt, std::true_type{});
-    for (; jt <= fb; ++jt) tile_step(jt, std::false_type{});
-    for (; jt <= jt1; ++jt) tile_step(jt, std::true_type{});
+    for (; jt <= jt1 && jt < fa; ++jt) tile_step(jt, std::true_type{}, dyn{});
+    // Unmasked tiles in pairs, so that each tile's LDS slot is a constant and
+    // its fragment reads take the slot offset as an immediate.
+    if (jt <= fb && ((jt - jt0) & 1)) tile_step(jt++, std::false_type{}, s1{});
+    for (; jt + 1 <= fb; jt += 2) {
+        tile_step(jt, std::false_type{}, s0{});
+        tile_step(jt + 1, std::false_type{}, s1{});
+    }
+    if (jt <= fb) tile_step(jt++, std::false_type{}, s0{});
+    for (; jt <= jt1; ++jt) tile_step(jt, std::true_type{}, dyn{});
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.f / l_tot;
