@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM-traffic summary of two rocprofv3 --pmc runs "
                          "(FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--relayout-profile", action="store_true",
+                    help="run only the relayout dispatches of RELAYOUT_PLAN (for rocprofv3) and exit")
+    ap.add_argument("--summarize-relayout", nargs=3, metavar=("TRACE_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="print per-dispatch time and HBM bytes of the --relayout-profile run "
+                         "from a rocprofv3 kernel trace and two --pmc runs, and exit")
     return ap.parse_args()
 
 
@@ -271,6 +276,136 @@ def summarize_trace(stats_csv):
     return "\n".join(out)
 
 
+# ---------------------------------------------------------------------------
+# Relayout dispatches under the profiler.  --relayout-profile launches, in this
+# order: a plain device copy of the relayout-bound buffer (the counters'
+# calibration), then two round trips of the relayout-bound workload (P=8,
+# N=262144, 32 heads, fused QKV), then two steps' worth of the 500K share's
+# rank-0 relayouts.  Every entry is one k_relayout dispatch; bytes are the
+# algorithmic read + write of that call.
+# ---------------------------------------------------------------------------
+def relayout_plan():
+    from synth import configs
+    w4, w5 = configs.WORKLOADS[4], configs.WORKLOADS[5]
+    full = w4.n_tokens * w4.relayout_groups * w4.relayout_heads * w4.head_dim * 2   # bytes
+    N, hq, hkv, d = w5.n_tokens, w5.hq, w5.hkv, w5.head_dim
+    q_share, kv_share = N * hq * d * 2, 2 * N * hkv * d * 2
+    plan = []
+    for _ in range(2):
+        plan += [("relayout-bound seq->head (all ranks)", "seq_to_head", 2 * full),
+                 ("relayout-bound head->seq (all ranks)", "head_to_seq", 2 * full)]
+    for _ in range(2):
+        plan += [("500k step: Q seq->head (rank 0)", "seq_to_head", 2 * q_share),
+                 ("500k step: K/V seq->head (rank 0)", "seq_to_head", 2 * kv_share),
+                 ("500k step: O head->seq (rank 0)", "head_to_seq", 2 * q_share),
+                 ("500k step: dO seq->head (rank 0)", "seq_to_head", 2 * q_share),
+                 ("500k step: dQ head->seq (rank 0)", "head_to_seq", 2 * q_share),
+                 ("500k step: dK/dV head->seq (rank 0)", "head_to_seq", 2 * kv_share)]
+    return plan, full
+
+
+def relayout_profile(dev):
+    import torch
+    from synth import configs
+    from ulysses_sequence_parallelism_share_amd import ops
+    w4, w5 = configs.WORKLOADS[4], configs.WORKLOADS[5]
+    x = to_dev_bf16(configs.relayout_inputs(w4), dev)
+    h = torch.empty((w4.sp_size, w4.relayout_groups, w4.n_tokens, w4.relayout_heads // w4.sp_size,
+                     w4.head_dim), dtype=torch.bfloat16, device=dev)
+    back = torch.empty_like(x)
+    back.copy_(x)                                   # the calibration copy
+    torch.cuda.synchronize()
+    for _ in range(2):
+        ops.ulysses_seq_to_head(x, out=h)
+        ops.ulysses_head_to_seq(h, w4.sp_size, out=back)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), x.view(torch.int16))
+    del x, h, back
+    torch.cuda.empty_cache()
+    P, N, hq, hkv, d = w5.sp_size, w5.n_tokens, w5.hq, w5.hkv, w5.head_dim
+    inp = configs.exchange_inputs(w5)
+    q_seq, kv_seq, do_seq = (to_dev_bf16(inp.pop(n), dev) for n in ("q_seq", "kv_seq", "do_seq"))
+    qh = torch.empty((1, N, hq, d), dtype=torch.bfloat16, device=dev)
+    kvh = torch.empty((2, N, hkv, d), dtype=torch.bfloat16, device=dev)
+    doh = torch.empty_like(qh)
+    o_seq, dq_seq, dkv_seq = (torch.zeros_like(t) for t in (q_seq, q_seq, kv_seq))
+    torch.cuda.synchronize()
+    for _ in range(2):
+        ops.ulysses_seq_to_head(q_seq, rank=0, out=qh)
+        ops.ulysses_seq_to_head(kv_seq, rank=0, out=kvh)
+        ops.ulysses_head_to_seq(qh, P, rank=0, out=o_seq)
+        ops.ulysses_seq_to_head(do_seq, rank=0, out=doh)
+        ops.ulysses_head_to_seq(doh, P, rank=0, out=dq_seq)
+        ops.ulysses_head_to_seq(kvh, P, rank=0, out=dkv_seq)
+    torch.cuda.synchronize()
+    log(f"[bench] relayout profile: {len(relayout_plan()[0])} relayout dispatches done")
+
+
+def _relayout_rows(path, value_col=None, counter=None):
+    """(dispatch_id, kernel name, value) of a rocprofv3 csv, ascending dispatch id; value is
+    the duration in ns (kernel trace) or the counter summed over its instances (KiB)."""
+    import csv
+    acc = {}
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if counter is not None and r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            if counter is None:
+                acc[key] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            else:
+                name, v = acc.get(key, (r["Kernel_Name"], 0.0))
+                acc[key] = (name, v + float(r["Counter_Value"]))
+    return [(k, *acc[k]) for k in sorted(acc)]
+
+
+def summarize_relayout(trace_csv, fetch_csv, write_csv):
+    plan, full = relayout_plan()
+    is_rel = re.compile(r"(^|[\s:\d])k_relayout([<(]|I[LZN])")
+    trace = [r for r in _relayout_rows(trace_csv) if is_rel.search(r[1])]
+    counts = {}
+    for c, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _relayout_rows(path, counter=c)
+        copies = [v for _, n, v in rows if "copy" in n.lower()]
+        rel = [v for _, n, v in rows if is_rel.search(n)]
+        counts[c] = (max(copies) if copies else None, rel)
+    if len(trace) != len(plan) or any(len(v[1]) != len(plan) for v in counts.values()):
+        raise SystemExit(f"expected {len(plan)} k_relayout dispatches, found {len(trace)} traced, "
+                         f"{[len(v[1]) for v in counts.values()]} counted")
+    out = ["# k_relayout per dispatch: kernel-trace duration and HBM bytes from rocprofv3 counters",
+           "# workloads: relayout-bound (P=8, N=262144, 32 heads, d=128, fused QKV [8][32768][3][32][128]",
+           "# bf16, 6 GiB each way) and the 500K-token rank share's rank-0 relayouts (N=524288,",
+           "# Q/dO/O/dQ: 32 global heads -> 4, K/V and dK/dV: 8 global KV heads -> 1, d=128)",
+           "# commands (GPU, from /tmp with TMPDIR=/tmp; REPO = the repository root):",
+           "#   rocprofv3 --kernel-trace --output-format csv -d REPO/gpurun_out/rl_trace -o run "
+           "-- python3 REPO/bench.py --relayout-profile",
+           "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d REPO/gpurun_out/rl_fetch -o run "
+           "-- python3 REPO/bench.py --relayout-profile",
+           "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d REPO/gpurun_out/rl_write -o run "
+           "-- python3 REPO/bench.py --relayout-profile",
+           "#   python3 REPO/bench.py --summarize-relayout REPO/gpurun_out/rl_trace/run_kernel_trace.csv "
+           "REPO/gpurun_out/rl_fetch/run_counter_collection.csv REPO/gpurun_out/rl_write/run_counter_collection.csv"]
+    half = full          # a plain copy of the relayout-bound buffer reads and writes `full` bytes
+    fc, wc = counts["FETCH_SIZE"][0], counts["WRITE_SIZE"][0]
+    f_fetch = half / (fc * 1024) if fc else None
+    f_write = half / (wc * 1024) if wc else None
+    out.append(f"# calibration copy ({half} bytes each way): FETCH_SIZE {fc} KiB -> factor "
+               f"{f_fetch}, WRITE_SIZE {wc} KiB -> factor {f_write}")
+    out.append("# read_bytes/write_bytes = counter KiB x 1024 x factor; algorithmic = read once + write once")
+    out.append(f"{'dispatch':<40}{'algo_GB':>9}{'ms':>9}{'GB/s':>9}{'%HBM':>7}"
+               f"{'fetch_KiB':>14}{'write_KiB':>14}{'read_GB':>9}{'write_GB':>9}{'counted/algo':>13}")
+    for i, (label, _, nbytes) in enumerate(plan):
+        ns = trace[i][2]
+        fk, wk = counts["FETCH_SIZE"][1][i], counts["WRITE_SIZE"][1][i]
+        rb = fk * 1024 * (f_fetch or 1.0)
+        wb = wk * 1024 * (f_write or 1.0)
+        gbs = nbytes / ns
+        out.append(f"{label:<40}{nbytes / 1e9:>9.3f}{ns / 1e6:>9.3f}{gbs:>9.1f}"
+                   f"{100 * gbs / PEAK_HBM_GBPS:>6.1f}%{fk:>14.1f}{wk:>14.1f}{rb / 1e9:>9.3f}"
+                   f"{wb / 1e9:>9.3f}{(rb + wb) / nbytes:>13.3f}")
+    return "\n".join(out)
+
+
 def relayout_bound(dev, reps):
     """The relayout-bound workload: P=8, N=262144, 32 heads, d=128, fused QKV (G=3),
     seq->head of all ranks then head->seq back, checked bit-exact on the device."""
@@ -403,6 +538,9 @@ def main():
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
         return
+    if args.summarize_relayout:
+        print(summarize_relayout(*args.summarize_relayout))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the all-to-all is emulated on one device); run with --gpus 1.", file=sys.stderr)
@@ -415,6 +553,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.relayout_profile:
+        relayout_profile(dev)
+        return
     w = configs.WORKLOADS[args.workload]
     P, N, hq, hkv, d = w.sp_size, w.n_tokens, w.hq, w.hkv, w.head_dim
     lengths = w.lengths()

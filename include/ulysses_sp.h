@@ -250,7 +250,8 @@ sp_status sp_attn_bwd_strided(const void *q, int64_t q_stride, const void *k, co
 
 /*
  * sp_linear_ce_workspace_bytes - workspace sp_linear_ce needs for this
- * vocabulary size and token chunk (0 for invalid sizes).
+ * vocabulary size and token chunk (0 for invalid sizes, including a vocab
+ * above 8421376).
  */
 size_t sp_linear_ce_workspace_bytes(int64_t vocab, int64_t chunk_tokens);
 
@@ -280,7 +281,9 @@ size_t sp_linear_ce_workspace_bytes(int64_t vocab, int64_t chunk_tokens);
  *                holds that many rows of fp32 logits and bf16 G
  *   workspace    >= sp_linear_ce_workspace_bytes(vocab, chunk_tokens) bytes,
  *                256-byte aligned
- * hidden must be a positive multiple of 256 (<= 65536), else SP_E_SHAPE.
+ * hidden must be a positive multiple of 256 (<= 65536) and vocab at most
+ * 8421376 (the 256-token tiles of G are addressed with 32-bit byte offsets:
+ * 255 rows of vocab rounded up to 256 bf16 values), else SP_E_SHAPE.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; fp32 log-sum-exp;
  * G rounded to bf16 for the two gradient products.  Deterministic.
  */

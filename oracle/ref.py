@@ -206,7 +206,7 @@ def allowed(seg: np.ndarray, rows: np.ndarray, cols: np.ndarray) -> np.ndarray:
 
 def _as_f64(x):
     x = np.asarray(x)
-    return bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+    return bf16_to_f64(x) if x.dtype == np.uint16 else np.asarray(x, dtype=np.float64)
 
 
 def _scale(d, softmax_scale):
@@ -352,6 +352,78 @@ def attn_key_cols(q, k, v, do, position_ids, cols, softmax_scale=None):
                 pos_c = cc - span[0]
                 dv[sel, kv] += P[:, pos_c].T @ do[rr, h]
                 dk[sel, kv] += scale * (dS[:, pos_c].T @ q[rr, h])
+    return dk, dv
+
+
+def attn_row_stats(q, k, v, do, position_ids, r0, r1, softmax_scale=None, block_rows=256):
+    """Per-row statistics of the query rows [r0, r1): the natural-log LSE of
+    each row's softmax, its output O and D_i = sum_e dO_ie O_ie (which equals
+    sum_j P_ij dP_ij, the row term of dS = P * (dP - D)).  Each row gets its
+    full softmax over all of its allowed keys, in blocks of consecutive rows
+    with the explicit mask over the block's key span.
+
+    Returns lse [hq][R], o [R][hq][d] and D [hq][R] (float64, R = r1 - r0)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    N, hq, d = q.shape
+    grp = hq // k.shape[1]
+    scale = _scale(d, softmax_scale)
+    seg = segment_ids(position_ids)
+    first = segment_first(position_ids)
+    R = r1 - r0
+    lse = np.zeros((hq, R))
+    o = np.zeros((R, hq, d))
+    D = np.zeros((hq, R))
+    for b0 in range(r0, r1, block_rows):
+        b1 = min(r1, b0 + block_rows)
+        rows = np.arange(b0, b1)
+        cols = np.arange(int(first[b0]), b1)
+        for h in range(hq):
+            kv = h // grp
+            P, m, l = _probs(q[:, h], k[:, kv], seg, rows, cols, scale)
+            ob = P @ v[cols, kv]
+            o[b0 - r0:b1 - r0, h] = ob
+            lse[h, b0 - r0:b1 - r0] = m + np.log(l)
+            D[h, b0 - r0:b1 - r0] = (do[rows, h] * ob).sum(axis=1)
+    return lse, o, D
+
+
+def attn_key_cols_from_stats(q, k, v, do, position_ids, cols, lse, D, softmax_scale=None,
+                             block_rows=1024):
+    """dK and dV of selected key columns from given row statistics.
+
+    Key j of KV head kh receives gradient from the query rows i >= j of its own
+    sample and every query head h sharing kh:
+        P_ij = exp(scale q_ih . k_j - LSE_hi),  dP_ij = dO_ih . v_j,
+        dV_j = sum_(h,i) P_ij dO_ih,  dK_j = scale sum_(h,i) P_ij (dP_ij - D_hi) q_ih.
+    ``lse`` and ``D`` are [hq][N] arrays (natural-log LSE and D = rowsum(dO * O)
+    of every query row); only the rows that see a requested column are read.
+    The rows are walked in blocks with the explicit mask of (rows x cols); each
+    column costs O(L d) for the L rows after it.  Returns dk, dv [C][hkv][d]."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    grp = hq // hkv
+    scale = _scale(d, softmax_scale)
+    seg = segment_ids(position_ids)
+    cols = np.asarray(cols, dtype=np.int64)
+    dk = np.zeros((cols.size, hkv, d))
+    dv = np.zeros((cols.size, hkv, d))
+    for s in np.unique(seg[cols]):
+        sel = np.flatnonzero(seg[cols] == s)
+        cc = cols[sel]
+        last = int(np.flatnonzero(seg == s)[-1])
+        for b0 in range(int(cc.min()), last + 1, block_rows):
+            rows = np.arange(b0, min(last + 1, b0 + block_rows))
+            mask = allowed(seg, rows, cc)
+            for h in range(hq):
+                kv = h // grp
+                S = scale * (q[rows, h] @ k[cc, kv].T)
+                S[~mask] = -np.inf
+                P = np.exp(S - lse[h, rows][:, None])
+                dP = do[rows, h] @ v[cc, kv].T
+                dS = P * (dP - D[h, rows][:, None])
+                dv[sel, kv] += P.T @ do[rows, h]
+                dk[sel, kv] += scale * (dS.T @ q[rows, h])
     return dk, dv
 
 

@@ -2,6 +2,8 @@
 patterns and the floating-point gates."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -12,10 +14,27 @@ MAX_ABS = 2e-2
 LSE_ABS = 2e-3
 
 
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MARGIN_LOG = os.path.join(_ROOT, "gpurun_out", "parity_margins.jsonl")
+
+
 def say(*a):
-    """Name the case on stdout (flushed) before a GPU step."""
-    print(*a, flush=True)
+    """Name the case on stdout (flushed) before a GPU step, and keep the line in
+    the parity log (pulled back with the run's outputs)."""
+    msg = " ".join(str(x) for x in a)
+    print(msg, flush=True)
     sys.stdout.flush()
+    _log({"msg": msg})
+
+
+def _log(rec):
+    rec = {"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], **rec}
+    try:
+        os.makedirs(os.path.dirname(MARGIN_LOG), exist_ok=True)
+        with open(MARGIN_LOG, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    except OSError:
+        pass
 
 
 def to_dev_bf16(bits: np.ndarray, device="cuda"):
@@ -56,7 +75,11 @@ def errors(got: np.ndarray, ref: np.ndarray):
 
 def gate(name: str, got, ref, rel_tol=REL_L2, abs_tol=MAX_ABS):
     rel, mx = errors(got, ref)
-    say(f"  {name}: relL2={'n/a (zero reference)' if rel is None else f'{rel:.3e}'} maxabs={mx:.3e}")
+    print(f"  {name}: relL2={'n/a (zero reference)' if rel is None else f'{rel:.3e}'} "
+          f"maxabs={mx:.3e}", flush=True)
+    _log({"gate": name, "relL2": rel, "maxabs": mx, "n": int(np.size(ref)),
+          "rel_tol": rel_tol, "abs_tol": abs_tol})
+    assert np.isfinite(ref).all(), f"{name}: non-finite reference"
     assert np.isfinite(got).all(), f"{name}: non-finite values"
     if rel is not None:      # an exactly-zero reference is gated on max abs alone
         assert rel <= rel_tol, f"{name}: relL2 {rel:.3e} > {rel_tol}"

@@ -268,3 +268,10 @@ def test_linear_ce_validation():
     p["x"] = MIS
     assert _lce(**p, ws=A16, wsb=need) == _lib.SP_E_ALIGN
     assert _lib.call("sp_linear_ce_workspace_bytes", 1000, 100) == 0
+    # 32-bit tile offsets: 255 rows of G at v_pad = 8421376 still fit, one more 256 does not
+    assert _lce(V=9_000_000) == _lib.SP_E_SHAPE
+    assert _lce(V=8_421_377) == _lib.SP_E_SHAPE
+    assert _lce(V=8_421_376) == _lib.SP_E_NULL
+    assert _lib.call("sp_linear_ce_workspace_bytes", 9_000_000, 128) == 0
+    assert _lib.call("sp_linear_ce_workspace_bytes", 8_421_376, 64) > 0
+    assert 255 * 8_421_376 * 2 + 127 < 2 ** 32 <= 255 * (8_421_376 + 256) * 2

@@ -10,6 +10,7 @@ import pytest
 from oracle import ref
 from synth import configs, gen
 
+import oracle_par
 from helpers import LSE_ABS, bits_of, errors, f64_of, gate, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -72,6 +73,61 @@ def test_attention_parity(name, N, hq, hkv, d, lens, scale):
         rel, mx = errors(f64_of(g), r)
         say(f"  {nm}: relL2={rel} maxabs={mx:.3e}")
         assert (rel is None and mx <= 1e-5) or (rel is not None and rel <= 1e-2)
+
+
+def _positions(kind, N, rng):
+    """position_ids the method's rule must handle (a sample starts at token 0 and
+    wherever the id is 0): ids that start above 0, skip values, or are negative."""
+    if kind == "nonzero-start":          # the first sample's ids start at 5000
+        return np.concatenate([np.arange(5000, 5000 + 700), np.arange(N - 700)]).astype(np.int64)
+    if kind == "non-consecutive":        # strictly increasing with gaps, zeros at two places
+        pos = np.cumsum(rng.integers(1, 9, N)).astype(np.int64)
+        pos[0], pos[333], pos[1100] = 0, 0, 0
+        return pos
+    if kind == "negative":               # ids below zero never start a sample
+        pos = np.arange(N, dtype=np.int64) - 400
+        pos[900] = 0
+        pos[1200:1260] = -7
+        return pos
+    if kind == "random-ids":             # arbitrary ids, about one in 200 a zero
+        pos = rng.integers(-3, 200, N).astype(np.int64)
+        return pos
+    raise ValueError(kind)
+
+
+POS_CASES = [  # name, N, hq, hkv, d, position kind, softmax_scale (0 = 1/sqrt(d))
+    ("pos-nonzero-start", 1500, 4, 1, 128, "nonzero-start", 0.0),
+    ("pos-non-consecutive", 1400, 4, 2, 128, "non-consecutive", 0.0),
+    ("pos-negative", 1600, 2, 1, 64, "negative", 0.0),
+    ("pos-random-ids", 1300, 4, 1, 128, "random-ids", 0.0),
+    # scale 1 at d = 128: raw scores ~ N(0, 128), so each row's maximum moves by far more
+    # than the forward's lazy-rescale threshold (2^8) again and again
+    ("peaked-softmax-scale1", 2000, 4, 1, 128, "nonzero-start", 1.0),
+    ("peaked-softmax-scale0.5-d64", 1111, 2, 2, 64, "non-consecutive", 0.5),
+]
+
+
+@pytest.mark.parametrize("name,N,hq,hkv,d,kind,scale", POS_CASES, ids=[c[0] for c in POS_CASES])
+def test_attention_position_ids_and_peaked_softmax(name, N, hq, hkv, d, kind, scale):
+    ops = _ops()
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    pos = _positions(kind, N, rng)
+    seg = ref.segment_ids(pos)
+    say(f"attention {name}: N={N} hq={hq} hkv={hkv} d={d} scale={scale} samples={seg[-1] + 1}")
+    q, k, v, do = _inputs(zlib.crc32(name.encode()) % 1000 + 1000, N, hq, hkv, d)
+    qd, kd, vd, dod = (to_dev_bf16(a) for a in (q, k, v, do))
+    posd = to_dev(pos)
+    o, lse = ops.sp_attn_fwd(qd, kd, vd, posd, softmax_scale=scale)
+    o_ref, lse_ref = ref.attn_fwd(q, k, v, pos, softmax_scale=scale or None)
+    gate("O", f64_of(o), o_ref)
+    lse_err = np.abs(f64_of(lse) - lse_ref).max()
+    say(f"  LSE maxabs={lse_err:.3e}")
+    assert lse_err <= LSE_ABS
+    dq, dk, dv = ops.sp_attn_bwd(qd, kd, vd, o, dod, lse, posd, softmax_scale=scale)
+    dq_r, dk_r, dv_r = ref.attn_bwd(q, k, v, do, pos, softmax_scale=scale or None)
+    gate("dQ", f64_of(dq), dq_r)
+    gate("dK", f64_of(dk), dk_r)
+    gate("dV", f64_of(dv), dv_r)
 
 
 def test_full_layer_tiny_sp4():
@@ -142,36 +198,75 @@ def test_llama3_8b_share_packed_full_oracle():
     gate("dV", f64_of(dv), dv_r)
 
 
-def _sample_rows(lens, N, rng, extra=96):
-    starts = np.cumsum([0] + list(lens[:-1]))
-    ends = starts + np.array(lens) - 1
-    tile_edges = np.concatenate([np.arange(0, N, 32)[1::max(1, N // 32 // 24)] + o for o in (-1, 0)])
-    rows = np.concatenate([starts, ends, tile_edges, rng.integers(0, N, extra)])
-    return np.unique(np.clip(rows, 0, N - 1))
+def _starts(lens):
+    return np.cumsum([0] + list(lens[:-1])).astype(np.int64)
 
 
-def _sample_cols(lens, width=48):
-    starts = np.cumsum([0] + list(lens[:-1]))
-    cols = [np.arange(s + L - min(width, L), s + L) for s, L in zip(starts, lens)]
-    return np.concatenate(cols)
+def _tile_edges(lo, hi, step, n_edges, rng):
+    """Up to n_edges multiples of `step` in (lo, hi), with the index on either side."""
+    edges = np.arange((lo // step + 1) * step, hi, step)
+    if edges.size > n_edges:
+        edges = np.sort(rng.choice(edges, n_edges, replace=False))
+    return np.concatenate([edges - 1, edges])
 
 
-def _sampled_check(q, k, v, do, pos, lens, o, lse, dq, dk, dv, seed):
-    N = pos.size
-    rng = np.random.default_rng(seed)
-    rows = _sample_rows(lens, N, rng)
+def _sample_rows(lens, rng, n_edges=1024, n_random=2304):
+    """>= 4096 query rows: every sample's first and last token, both sides of 128-token
+    tile edges, and random rows."""
+    starts = _starts(lens)
+    N = int(sum(lens))
+    rows = [starts, starts + np.array(lens) - 1, _tile_edges(0, N, 128, n_edges, rng),
+            rng.integers(0, N, n_random)]
+    return np.unique(np.clip(np.concatenate(rows), 0, N - 1))
+
+
+def _sample_cols_span(lo, hi, n_target, rng):
+    """Key columns in [lo, hi): the first 128, both sides of 128-key tile edges, the
+    last key, and random keys, about n_target in all."""
+    first = np.arange(lo, min(hi, lo + 128))
+    edges = _tile_edges(lo, hi, 128, max(1, n_target // 4), rng)
+    rand = rng.integers(lo, hi, max(1, n_target - first.size - edges.size))
+    return np.unique(np.concatenate([first, edges, rand, [hi - 1]]))
+
+
+def _par_progress(msg):
+    say(f"  {msg}")
+
+
+def _widen(x):
+    return ref.bf16_to_f64(x) if x.dtype == np.uint16 else np.asarray(x, np.float64)
+
+
+def _deep_check(q, k, v, do, pos, o, lse, dq, dk, dv, stat_ranges, rows, cols):
+    """O and LSE at every row of `stat_ranges` (all-row fp64 statistics), dQ at `rows`,
+    dK/dV at `cols` (from those statistics; every row that sees a column must lie in
+    `stat_ranges`)."""
+    q, k, v, do = (_widen(a) for a in (q, k, v, do))
+    N, hq, _ = q.shape
+    lse_all = np.full((hq, N), np.nan)
+    D_all = np.full((hq, N), np.nan)
+    o_g, lse_g = f64_of(o), f64_of(lse)
+    for r0, r1 in stat_ranges:
+        say(f"  oracle row statistics for rows [{r0}, {r1})")
+        l_r, o_r, D_r = oracle_par.row_stats(q, k, v, do, pos, r0, r1, progress=_par_progress)
+        lse_all[:, r0:r1], D_all[:, r0:r1] = l_r, D_r
+        gate(f"O rows [{r0},{r1})", o_g[r0:r1], o_r)
+        lerr = float(np.abs(lse_g[:, r0:r1] - l_r).max())
+        say(f"  LSE rows [{r0},{r1}) maxabs={lerr:.3e}")
+        assert lerr <= LSE_ABS
     say(f"  sampled rows: {rows.size}")
-    o_r, lse_r, dq_r = ref.attn_rows(q, k, v, do, pos, rows)
-    gate("O rows", f64_of(o)[rows], o_r)
-    assert np.abs(f64_of(lse)[:, rows] - lse_r).max() <= LSE_ABS
+    _, _, dq_r = oracle_par.rows(q, k, v, do, pos, rows, progress=_par_progress)
     gate("dQ rows", f64_of(dq)[rows], dq_r)
-    cols = _sample_cols(lens)
     say(f"  sampled key columns: {cols.size}")
-    dk_r, dv_r = ref.attn_key_cols(q, k, v, do, pos, cols)
+    dk_r, dv_r = oracle_par.key_cols(q, k, v, do, pos, cols, lse_all, D_all, progress=_par_progress)
     dk_g, dv_g = f64_of(dk), f64_of(dv)
     gate("dK cols", dk_g[cols], dk_r)
     gate("dV cols", dv_g[cols], dv_r)
-    # invariants at full size, per sample: sum_j dV_j = sum_i sum_(heads) dO_i; sum_j dK_j = 0
+    return dk_g, dv_g
+
+
+def _sum_invariants(do, lens, dk_g, dv_g):
+    """Per sample, at full size: sum_j dV_j = sum_i sum_(heads) dO_i; sum_j dK_j = 0."""
     do64 = ref.bf16_to_f64(do)
     s = 0
     for L in lens:
@@ -187,10 +282,15 @@ def _sampled_check(q, k, v, do, pos, lens, o, lse, dq, dk, dv, seed):
 
 
 @pytest.mark.slow
-def test_long_sequence_share_sampled():
-    """Single long sequence at sp_size 8: N=131072, 4 query heads / 1 KV head, d=128."""
+@pytest.mark.timeout(900)
+def test_long_sequence_share_deep():
+    """Single long sequence at sp_size 8: N=131072, 4 query heads / 1 KV head, d=128.
+    O and LSE at every row; dQ at >= 4096 rows; dK/dV at >= 4096 key columns over the
+    whole sequence (keys 0-127 and both sides of 128-key tile edges included), each
+    against fp64 sums over every query row that sees it (up to 4 x 131072 rows)."""
     ops = _ops()
     w = configs.WORKLOADS[3]
+    N = w.n_tokens
     say(f"workload {w.name}")
     inp = configs.rank_share_inputs(w)
     q, k, v, do, pos = inp["q"], inp["k"], inp["v"], inp["do"], inp["pos"]
@@ -198,11 +298,17 @@ def test_long_sequence_share_sampled():
     posd = to_dev(pos)
     o, lse = ops.sp_attn_fwd(qd, kd, vd, posd)
     dq, dk, dv = ops.sp_attn_bwd(qd, kd, vd, o, dod, lse, posd)
-    _sampled_check(q, k, v, do, pos, w.lengths(), o, lse, dq, dk, dv, seed=3)
+    rng = np.random.default_rng(3)
+    rows = _sample_rows(w.lengths(), rng)
+    cols = _sample_cols_span(0, N, 4160, rng)
+    assert rows.size >= 4096 and cols.size >= 4096
+    dk_g, dv_g = _deep_check(q, k, v, do, pos, o, lse, dq, dk, dv, [(0, N)], rows, cols)
+    _sum_invariants(do, w.lengths(), dk_g, dv_g)
 
 
 @pytest.mark.slow
-def test_500k_share_through_relayout_sampled():
+@pytest.mark.timeout(900)
+def test_500k_share_through_relayout_deep():
     """500K-token rank share at sp_size 8 (4 query / 1 KV head, d=128, 4 packed samples),
     in the launch configuration the benchmark times: rank 0's share is gathered from the
     sequence-sharded Q, KV and dO buffers by the seq->head relayout, and O and the
@@ -234,4 +340,20 @@ def test_500k_share_through_relayout_sampled():
     assert np.array_equal(o_back, bits_of(o))
     del o_seq
     torch.cuda.empty_cache()
-    _sampled_check(q, k, v, do, pos, w.lengths(), o, lse, dq, dk, dv, seed=5)
+    # O/LSE statistics: the whole 37964-token sample and the last 4096 rows of each other
+    # sample; dK/dV over the whole 37964-token sample and in the last 4096 keys of the others
+    lens = w.lengths()
+    starts = _starts(lens)
+    ends = starts + np.array(lens)
+    rng = np.random.default_rng(5)
+    full_s = int(np.argmin(lens))
+    ranges, cols = [], []
+    for i, (s0, s1) in enumerate(zip(starts, ends)):
+        lo = int(s0) if i == full_s else int(s1) - 4096
+        ranges.append((lo, int(s1)))
+        cols.append(_sample_cols_span(lo, int(s1), 3072 if i == full_s else 512, rng))
+    cols = np.unique(np.concatenate(cols))
+    rows = _sample_rows(lens, rng)
+    assert rows.size >= 4096 and cols.size >= 4096
+    dk_g, dv_g = _deep_check(q, k, v, do, pos, o, lse, dq, dk, dv, ranges, rows, cols)
+    _sum_invariants(do, lens, dk_g, dv_g)

@@ -500,6 +500,101 @@ def test_sampled_rows_and_cols_match_full():
     np.testing.assert_allclose(dv_s, dv[cols], rtol=1e-11, atol=1e-12)
 
 
+def test_row_stats_match_forward_and_closed_forms():
+    """LSE and O of attn_row_stats equal the (brute-force pinned) forward on any row
+    range; D has closed forms: with every V row equal to c, O_i = c and D_i = dO_i . c;
+    with scale 0, O_i is the mean of V over [start, i] and D_i = dO_i . that mean."""
+    lens = [45, 1, 80, 30]
+    N, hq, hkv, d = sum(lens), 4, 2, 16
+    q, k, v, do = (_rand(40 + i, sh) for i, sh in
+                   enumerate(((N, hq, d), (N, hkv, d), (N, hkv, d), (N, hq, d))))
+    pos = gen.position_ids_from_lengths(lens)
+    o, lse = ref.attn_fwd(q, k, v, pos, softmax_scale=0.4)
+    for r0, r1, blk in ((0, N, 256), (3, 130, 7), (46, 47, 1), (100, N, 64)):
+        l_s, o_s, D_s = ref.attn_row_stats(q, k, v, do, pos, r0, r1, softmax_scale=0.4, block_rows=blk)
+        np.testing.assert_allclose(l_s, lse[:, r0:r1], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(o_s, o[r0:r1], rtol=1e-12, atol=1e-13)
+        assert D_s.shape == (hq, r1 - r0)
+    c = _rand(50, (d,))
+    vc = np.tile(c, (N, hkv, 1))
+    _, o_c, D_c = ref.attn_row_stats(q, k, vc, do, pos, 0, N, block_rows=33)
+    np.testing.assert_allclose(o_c, np.broadcast_to(c, o_c.shape), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(D_c, (do @ c).T, rtol=1e-11, atol=1e-12)
+    _, _, D_0 = ref.attn_row_stats(q, k, v, do, pos, 0, N, softmax_scale=0.0, block_rows=17)
+    first = ref.segment_first(pos)
+    for i in (0, 44, 45, 46, 47, 100, N - 1):
+        for h in range(hq):
+            mean = v[first[i]:i + 1, h // 2].mean(axis=0)
+            assert abs(D_0[h, i] - float(do[i, h] @ mean)) < 1e-12
+
+
+@pytest.mark.parametrize("lens,hq,hkv", [([70, 3, 100, 37], 4, 2), ([1, 64, 1, 130], 3, 1),
+                                         ([211], 2, 2)])
+def test_key_cols_from_stats_match_full_backward(lens, hq, hkv):
+    """dK/dV of chosen key columns, from all-row statistics, equal the full backward's
+    (itself pinned by finite differences) at those columns, with GQA and packing."""
+    N, d = sum(lens), 8
+    q, k, v, do = (gen.normal_bf16((61, s), sh) for s, sh in
+                   ((1, (N, hq, d)), (2, (N, hkv, d)), (3, (N, hkv, d)), (4, (N, hq, d))))
+    pos = gen.position_ids_from_lengths(lens)
+    _, dk, dv = ref.attn_bwd(q, k, v, do, pos, softmax_scale=0.7, block_rows=32)
+    lse, _, D = ref.attn_row_stats(q, k, v, do, pos, 0, N, softmax_scale=0.7, block_rows=40)
+    cols = np.arange(N)
+    dk_s, dv_s = ref.attn_key_cols_from_stats(q, k, v, do, pos, cols, lse, D, softmax_scale=0.7,
+                                              block_rows=13)
+    np.testing.assert_allclose(dk_s, dk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv_s, dv, rtol=1e-10, atol=1e-12)
+    some = np.array(sorted({0, N - 1, N // 2, lens[0] - 1, min(N - 1, lens[0])}))
+    dk_p, dv_p = ref.attn_key_cols_from_stats(q, k, v, do, pos, some, lse, D, softmax_scale=0.7)
+    np.testing.assert_allclose(dk_p, dk[some], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv_p, dv[some], rtol=1e-10, atol=1e-12)
+    # a wrong D (one row's value moved) must change some key's dK
+    D_bad = D.copy()
+    D_bad[0, N - 1] += 1.0
+    dk_b, _ = ref.attn_key_cols_from_stats(q, k, v, do, pos, cols, lse, D_bad, softmax_scale=0.7)
+    assert np.abs(dk_b - dk).max() > 1e-6
+
+
+def test_bf16_widening_all_patterns_against_torch():
+    """bf16_to_f64 over all 65536 bit patterns equals torch's bf16 -> float64
+    conversion (NaN compared by class: both NaN), plus hand-worked values."""
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):          # signalling-NaN patterns widen to NaN
+        ours = ref.bf16_to_f64(bits)
+    theirs = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan_o, nan_t = np.isnan(ours), np.isnan(theirs)
+    assert np.array_equal(nan_o, nan_t) and nan_o.sum() == 2 * 127
+    assert np.array_equal(ours[~nan_o], theirs[~nan_t])
+    assert np.array_equal(np.signbit(ours[~nan_o]), np.signbit(theirs[~nan_t]))   # -0 stays -0
+    hand = {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126,
+            0x7F7F: (2 - 2 ** -7) * 2.0 ** 127, 0x7F80: math.inf, 0xFF80: -math.inf,
+            0x3E80: 0.25, 0x4049: 3.140625}
+    for b, val in hand.items():
+        assert ref.bf16_to_f64(np.array([b], np.uint16))[0] == val
+    assert ref.bf16_to_f64(np.array([0x8000], np.uint16))[0] == 0.0
+    assert np.signbit(ref.bf16_to_f64(np.array([0x8000], np.uint16))[0])
+
+
+@pytest.mark.parametrize("P,T,G,H,d,r,g0,g1", [(2, 3, 3, 4, 2, 1, 0, 3), (4, 2, 3, 8, 3, 2, 1, 3),
+                                               (8, 2, 1, 8, 2, 0, 0, 1), (3, 4, 2, 6, 1, 2, 1, 2)])
+def test_gather_share_is_rank_slice_of_relayout(P, T, G, H, d, r, g0, g1):
+    """gather_share(x, r, g0, g1) equals rank r's seq->head share, groups [g0, g1),
+    moved to token-major [N][G'][H/P][d]; checked by element tags against brute-force
+    index loops too."""
+    x, tok, grp, head, e = _tagged(P, T, G, H, d)
+    got = ref.gather_share(x, r, g0, g1)
+    want = np.ascontiguousarray(ref.seq_to_head(x, rank=r)[g0:g1].transpose(1, 0, 2, 3))
+    assert got.shape == (P * T, g1 - g0, H // P, d)
+    assert np.array_equal(got, want)
+    hl = H // P
+    for n in range(P * T):
+        for gi in range(g1 - g0):
+            for j in range(hl):
+                for ee in range(d):
+                    assert got[n, gi, j, ee] == (((n * G + g0 + gi) * H + r * hl + j) * d) + ee
+
+
 # ---------------------------------------------------------------------------
 # Token-weighted loss
 # ---------------------------------------------------------------------------

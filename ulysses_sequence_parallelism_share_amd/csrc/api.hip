@@ -69,6 +69,12 @@ inline bool bad_stride(int64_t stride, int heads, int d) {
     return stride < (int64_t)heads * d || stride % 8 != 0 || stride > kMaxStride;
 }
 
+// The cross-entropy's dX product stages 256-token rows of the bf16 softmax
+// gradient G ([chunk][vocab rounded up to 256]) with 32-bit byte offsets from
+// the tile base: 255 * v_pad * 2 + 127 must stay below 2^32, which holds for
+// v_pad <= 8421376 (a multiple of 256), so the vocabulary is limited to that.
+constexpr int64_t kMaxLceVocab = 8421376;
+
 inline int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -243,7 +249,7 @@ sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o
 }
 
 size_t sp_linear_ce_workspace_bytes(int64_t vocab, int64_t chunk_tokens) {
-    if (vocab < 1 || vocab >= ((int64_t)1 << 30) || chunk_tokens < 64 || chunk_tokens % 64 != 0 ||
+    if (vocab < 1 || vocab > kMaxLceVocab || chunk_tokens < 64 || chunk_tokens % 64 != 0 ||
         chunk_tokens >= ((int64_t)1 << 24))
         return 0;
     return lce_workspace_layout(vocab, chunk_tokens, nullptr, nullptr);
@@ -254,7 +260,7 @@ sp_status sp_linear_ce(const void *x, const void *w, const int64_t *labels, int6
                        int grad_dtype, float *token_loss, float *lse, void *dx, float *dw,
                        int64_t chunk_tokens, void *workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-    if (n_tokens < 0 || vocab < 1 || vocab >= ((int64_t)1 << 30) || hidden < 256 ||
+    if (n_tokens < 0 || vocab < 1 || vocab > kMaxLceVocab || hidden < 256 ||
         hidden % 256 != 0 || hidden > 65536 || n_tokens >= ((int64_t)1 << 31))
         return SP_E_SHAPE;
     if (chunk_tokens < 64 || chunk_tokens % 64 != 0 || chunk_tokens >= ((int64_t)1 << 24))
