@@ -258,14 +258,21 @@ def attn_fwd(q, k, v, position_ids, softmax_scale=None, block_rows=256):
     return o, lse
 
 
-def attn_bwd(q, k, v, do, position_ids, softmax_scale=None, block_rows=256):
+def attn_bwd(q, k, v, do, position_ids, softmax_scale=None, block_rows=256, o=None):
     """Gradients of sum(dO * O) with respect to q, k, v (float64).
 
     With P the attention probabilities: dV = P^T dO, dP = dO v^T,
     D_i = sum_j P_ij dP_ij, dS = P * (dP - D), dQ = scale dS k,
     dK = scale dS^T q; dK/dV of a KV head sum over the query heads that
-    share it."""
+    share it.
+
+    ``o`` (optional, [N][hq][d], bf16 bits or floats): a stored forward output
+    to form D from instead, D_i = sum_e dO_ie o_ie, the way a backward that is
+    handed the layer's output computes it.  With the exact output this is the
+    same D (sum_j P_ij dP_ij = dO_i . sum_j P_ij v_j); with a rounded one it is
+    the gradient such a backward reaches."""
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    o = None if o is None else _as_f64(o)
     N, hq, d = q.shape
     hkv = k.shape[1]
     grp = hq // hkv
@@ -282,7 +289,10 @@ def attn_bwd(q, k, v, do, position_ids, softmax_scale=None, block_rows=256):
             P, _, _ = _probs(qh, kh, seg, rows, cols, scale)
             dv[cols, kv] += P.T @ doh[rows]
             dP = doh[rows] @ vh[cols].T
-            D = (P * dP).sum(axis=1, keepdims=True)
+            if o is None:
+                D = (P * dP).sum(axis=1, keepdims=True)
+            else:
+                D = (doh[rows] * o[rows, h]).sum(axis=1, keepdims=True)
             dS = P * (dP - D)
             dq[rows, h] = scale * (dS @ kh[cols])
             dk[cols, kv] += scale * (dS.T @ qh[rows])

@@ -11,7 +11,7 @@ import numpy as np
 # Gates for bf16 inputs against the fp64 oracle: relative L2 and max abs error.
 REL_L2 = 5e-3
 MAX_ABS = 2e-2
-LSE_ABS = 2e-3
+LSE_ABS = 1e-3
 
 
 _ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -449,6 +449,31 @@ def test_bwd_finite_differences():
         assert err < 1e-7, (name, err)
 
 
+def test_bwd_with_given_output():
+    """D formed from a given output: the exact output gives the exact backward; an output
+    off by delta_i moves D_i by dO_i . delta_i and dQ_i by -scale (dO_i . delta_i) sum_j P_ij k_j."""
+    lens = [9, 1, 14]
+    N, hq, hkv, d = sum(lens), 4, 2, 6
+    q, k, v, do = _rand(60, (N, hq, d)), _rand(61, (N, hkv, d)), _rand(62, (N, hkv, d)), _rand(63, (N, hq, d))
+    pos = gen.position_ids_from_lengths(lens)
+    o, _ = ref.attn_fwd(q, k, v, pos, softmax_scale=0.6)
+    want = ref.attn_bwd(q, k, v, do, pos, softmax_scale=0.6)
+    got = ref.attn_bwd(q, k, v, do, pos, softmax_scale=0.6, o=o, block_rows=5)
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+    delta = np.zeros_like(o)
+    delta[12, 1] = _rand(64, (d,))
+    dq2, _, _ = ref.attn_bwd(q, k, v, do, pos, softmax_scale=0.6, o=o + delta)
+    # row 12 (sample 3, keys 10..12), head 1 uses KV head 0: sum_j P_ij k_j is the output
+    # of attention with v replaced by k
+    ok, _ = ref.attn_fwd(q, k, k, pos, softmax_scale=0.6)
+    shift = -0.6 * float(do[12, 1] @ delta[12, 1]) * ok[12, 1]
+    np.testing.assert_allclose(dq2[12, 1] - want[0][12, 1], shift, rtol=1e-10, atol=1e-13)
+    others = np.ones(N, bool)
+    others[12] = False
+    np.testing.assert_allclose(dq2[others], want[0][others], rtol=1e-12, atol=1e-14)
+
+
 def test_bwd_gqa_equals_replicated_sum():
     N, hq, hkv, d = 33, 6, 2, 8
     grp = hq // hkv
