@@ -51,7 +51,8 @@ typedef enum sp_status {
     SP_E_RANK = 5,           /* rank outside [-1, sp_size) */
     SP_E_WORKSPACE = 6,      /* workspace NULL or smaller than sp_attn_workspace_bytes() */
     SP_E_HIP = 7,            /* a HIP launch failed */
-    SP_E_DTYPE = 8           /* unknown sp_dtype */
+    SP_E_DTYPE = 8,          /* unknown sp_dtype */
+    SP_E_SCRATCH = 9         /* sp_attn_bwd_noalloc: more scratch than its fixed array holds */
 } sp_status;
 
 typedef enum sp_dtype {
@@ -214,6 +215,31 @@ sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o
                       int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
                       float softmax_scale, int grad_dtype, void *dq, void *dk, void *dv,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sp_attn_bwd_noalloc - sp_attn_bwd without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  It allocates nothing:
+ * the workspace comes from a fixed device array of 32 MiB inside the library
+ * (one per GPU, held until the process ends; its device address is looked up
+ * on the first call on each device).
+ *
+ * Arguments, layouts, arithmetic and results are those of sp_attn_bwd, bit
+ * for bit.  The backward's part of the workspace must fit the array: with
+ * M = n_tokens * (n_q_heads / n_kv_heads) rounded up to 64, about
+ * 8 * n_tokens + 8 * n_kv_heads * M bytes (plus 4 * n_kv_heads * head_dim * M
+ * when n_q_heads / n_kv_heads does not divide 32), e.g. 20 MiB for 524288
+ * tokens with 4 query heads and 1 KV head; a larger call returns SP_E_SCRATCH
+ * before anything touches the device.  Every call on one GPU uses that GPU's
+ * array (nothing in it needs to start at zero): calls that overlap on one GPU,
+ * on different streams or from different threads, race and give undefined
+ * results.  The current HIP device must be the one `stream` belongs to.
+ */
+sp_status sp_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                              const void *d_o, const float *lse, const int64_t *position_ids,
+                              int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                              float softmax_scale, int grad_dtype, void *dq, void *dk, void *dv,
+                              hipStream_t stream);
 
 /*
  * sp_attn_fwd_strided, sp_attn_bwd_strided - sp_attn_fwd and sp_attn_bwd on

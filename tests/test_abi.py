@@ -25,7 +25,7 @@ def test_library_exports_every_header_function():
 
 
 def test_status_strings():
-    for s in range(0, 9):
+    for s in range(0, 10):
         assert _lib.status_string(s)
     assert _lib.status_string(99) == "unknown status"
 
@@ -117,6 +117,42 @@ def test_attention_validation():
         assert fn(**ptrs, ws=MIS, wsb=need) == _lib.SP_E_ALIGN
     assert _bwd(gd=7) == _lib.SP_E_DTYPE
     assert _bwd(gd=7, N=0) == _lib.SP_E_DTYPE
+
+
+def _bwd_na(**kw):
+    a = dict(q=None, k=None, v=None, o=None, do=None, lse=None, pos=None, N=256, hq=4, hkv=1,
+             d=128, scale=0.0, gd=1, dq=None, dk=None, dv=None)
+    a.update(kw)
+    return _lib.call("sp_attn_bwd_noalloc", a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                     a["pos"], a["N"], a["hq"], a["hkv"], a["d"], a["scale"], a["gd"], a["dq"],
+                     a["dk"], a["dv"], None)
+
+
+def test_noalloc_backward_validation():
+    """The allocation-free backward checks its arguments like sp_attn_bwd, and rejects a
+    problem whose workspace exceeds its fixed 32 MiB device array before touching the
+    device (so these calls work without a GPU)."""
+    fn = _bwd_na
+    assert fn() == _lib.SP_E_NULL
+    assert fn(d=96) == _lib.SP_E_SHAPE
+    assert fn(hq=6, hkv=4) == _lib.SP_E_NOT_DIVISIBLE
+    assert fn(scale=float("nan")) == _lib.SP_E_SHAPE
+    assert fn(gd=7) == _lib.SP_E_DTYPE
+    assert fn(N=0) == _lib.SP_OK
+    p = dict(BWD_PTRS)
+    p["q"] = MIS
+    assert fn(**p) == _lib.SP_E_ALIGN
+    # the 500K-token share (4 query heads, 1 KV head) fits: 8 bytes per token of segment
+    # bounds, 8 per virtual row of statistics, about 20 MiB
+    assert fn(N=524288, hq=4, hkv=1) == _lib.SP_E_NULL
+    # 2^20 tokens with 8 query heads per KV head need 8 N + 64 N bytes: too much, refused
+    # even with valid-looking pointers
+    assert fn(**BWD_PTRS, N=1 << 20, hq=8, hkv=1) == _lib.SP_E_SCRATCH
+    assert fn(N=1 << 20, hq=8, hkv=1) == _lib.SP_E_SCRATCH
+    # a gathered-rows problem (3 query heads per KV head) also needs the row copies
+    assert fn(**BWD_PTRS, N=40000, hq=3, hkv=1, d=128) == _lib.SP_E_SCRATCH
+    assert fn(N=10000, hq=3, hkv=1, d=128) == _lib.SP_E_NULL
+    assert "scratch" in _lib.status_string(_lib.SP_E_SCRATCH)
 
 
 def test_workspace_bytes():

@@ -20,6 +20,7 @@ SP_E_RANK = 5
 SP_E_WORKSPACE = 6
 SP_E_HIP = 7
 SP_E_DTYPE = 8
+SP_E_SCRATCH = 9
 SP_DTYPE_BF16 = 0
 SP_DTYPE_F32 = 1
 
@@ -36,6 +37,8 @@ SIGNATURES = {
     "sp_attn_fwd": (_i, [_vp, _vp, _vp, _vp, _i64, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
     "sp_attn_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i, _i, _i, _f, _i, _vp, _vp,
                          _vp, _vp, _sz, _vp]),
+    "sp_attn_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i, _i, _i, _f, _i,
+                                 _vp, _vp, _vp, _vp]),
     "sp_attn_fwd_strided": (_i, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i, _i, _i, _f, _vp, _i64,
                                  _vp, _vp, _sz, _vp]),
     "sp_attn_bwd_strided": (_i, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64,

@@ -7,6 +7,8 @@
 // "Configuration"); masking comes from position_ids only.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/ulysses_sp.h"
 #include "launch.h"
 
@@ -80,7 +82,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws) {
+size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws,
+                             bool with_vt) {
     const int g = hq / hkv;
     const int64_t Mpad = pad64(N * g);
     size_t off = 0;
@@ -98,10 +101,95 @@ size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, Attn
     w.qv = gather ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
     w.dov = gather ? take(2 * (size_t)hkv * d * Mpad) : nullptr;
     w.rowstat = (float *)take(8 * (size_t)hkv * Mpad);
-    w.vt = take(2 * (size_t)hkv * d * pad64(N));
+    w.vt = with_vt ? take(2 * (size_t)hkv * d * pad64(N)) : nullptr;
     if (ws) *ws = w;
     return off;
 }
+
+// ---------------------------------------------------------------------------
+// Fixed device scratch for sp_attn_bwd_noalloc: the backward's workspace
+// (segment bounds, row statistics, gathered rows) taken from this array
+// instead of a caller buffer.  Every GPU the library runs on holds its own
+// copy at its own address for the life of the process.  In host code the
+// array's name is only a stand-in for the symbol, so its device address is
+// looked up once per device with hipGetSymbolAddress and kept; kernels get
+// that address.  No part of the scratch needs to start at zero (the segment
+// pass, the row-statistics pass and the row gather write everything the
+// later kernels read), and calls that overlap on one GPU share, and race on,
+// the array.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on its first use).
+hipError_t scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+// Checks and launches of the backward, shared by the workspace and the
+// scratch entry points.  With `workspace` NULL and use_scratch set, the
+// workspace comes from the device's scratch array.
+sp_status attn_bwd_checked(const void *q, int64_t q_stride, const void *k, const void *v,
+                           int64_t kv_stride, const void *o, int64_t o_stride, const void *d_o,
+                           int64_t do_stride, const float *lse, const int64_t *position_ids,
+                           int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                           float softmax_scale, int grad_dtype, void *dq, int64_t dq_stride,
+                           void *dk, int64_t dk_stride, void *dv, int64_t dv_stride,
+                           void *workspace, size_t workspace_bytes, bool use_scratch,
+                           hipStream_t stream) {
+    sp_status st = check_attn_shape(n_tokens, n_q_heads, n_kv_heads, head_dim, softmax_scale);
+    if (st != SP_OK) return st;
+    if (grad_dtype != SP_DTYPE_BF16 && grad_dtype != SP_DTYPE_F32) return SP_E_DTYPE;
+    if (bad_stride(q_stride, n_q_heads, head_dim) || bad_stride(kv_stride, n_kv_heads, head_dim) ||
+        bad_stride(o_stride, n_q_heads, head_dim) || bad_stride(do_stride, n_q_heads, head_dim) ||
+        bad_stride(dq_stride, n_q_heads, head_dim) || bad_stride(dk_stride, n_kv_heads, head_dim) ||
+        bad_stride(dv_stride, n_kv_heads, head_dim))
+        return SP_E_SHAPE;
+    // the scratch must hold the backward's part of the workspace (checked
+    // before anything touches the device)
+    const size_t need = attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, nullptr,
+                                              nullptr, !use_scratch);
+    if (use_scratch && need > kNoAllocScratchBytes) return SP_E_SCRATCH;
+    if (n_tokens == 0) return SP_OK;
+    if (!q || !k || !v || !o || !d_o || !lse || !position_ids || !dq || !dk || !dv) return SP_E_NULL;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+        misaligned(d_o, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
+        misaligned(position_ids, 8) || misaligned(lse, 4))
+        return SP_E_ALIGN;
+    if (use_scratch) {
+        if (scratch_address(&workspace) != hipSuccess) return SP_E_HIP;
+    } else {
+        if (!workspace || workspace_bytes < need) return SP_E_WORKSPACE;
+        if (misaligned(workspace, 16)) return SP_E_ALIGN;
+    }
+    AttnWorkspace ws;
+    attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, workspace, &ws, !use_scratch);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
+    const AttnStrides strides{q_stride, kv_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride};
+    return launch_attn_bwd(q, k, v, o, d_o, lse, position_ids, n_tokens, n_q_heads, n_kv_heads,
+                           head_dim, scale, grad_dtype == SP_DTYPE_F32, dq, dk, dv, strides, ws,
+                           stream) == hipSuccess ? SP_OK : SP_E_HIP;
+}
+
+}  // namespace
 
 #pragma GCC visibility push(default)
 extern "C" {
@@ -117,6 +205,7 @@ const char *sp_status_string(int status) {
         case SP_E_WORKSPACE: return "workspace missing or too small";
         case SP_E_HIP: return "a HIP launch failed";
         case SP_E_DTYPE: return "unknown element type";
+        case SP_E_SCRATCH: return "the call needs more scratch than the library's fixed device array holds";
         default: return "unknown status";
     }
 }
@@ -211,30 +300,10 @@ sp_status sp_attn_bwd_strided(const void *q, int64_t q_stride, const void *k, co
                               float softmax_scale, int grad_dtype, void *dq, int64_t dq_stride,
                               void *dk, int64_t dk_stride, void *dv, int64_t dv_stride,
                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    sp_status st = check_attn_shape(n_tokens, n_q_heads, n_kv_heads, head_dim, softmax_scale);
-    if (st != SP_OK) return st;
-    if (grad_dtype != SP_DTYPE_BF16 && grad_dtype != SP_DTYPE_F32) return SP_E_DTYPE;
-    if (bad_stride(q_stride, n_q_heads, head_dim) || bad_stride(kv_stride, n_kv_heads, head_dim) ||
-        bad_stride(o_stride, n_q_heads, head_dim) || bad_stride(do_stride, n_q_heads, head_dim) ||
-        bad_stride(dq_stride, n_q_heads, head_dim) || bad_stride(dk_stride, n_kv_heads, head_dim) ||
-        bad_stride(dv_stride, n_kv_heads, head_dim))
-        return SP_E_SHAPE;
-    if (n_tokens == 0) return SP_OK;
-    if (!q || !k || !v || !o || !d_o || !lse || !position_ids || !dq || !dk || !dv) return SP_E_NULL;
-    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
-        misaligned(d_o, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
-        misaligned(position_ids, 8) || misaligned(lse, 4))
-        return SP_E_ALIGN;
-    const size_t need = attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, nullptr, nullptr);
-    if (!workspace || workspace_bytes < need) return SP_E_WORKSPACE;
-    if (misaligned(workspace, 16)) return SP_E_ALIGN;
-    AttnWorkspace ws;
-    attn_workspace_layout(n_tokens, n_q_heads, n_kv_heads, head_dim, workspace, &ws);
-    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)head_dim);
-    const AttnStrides strides{q_stride, kv_stride, o_stride, do_stride, dq_stride, dk_stride, dv_stride};
-    return launch_attn_bwd(q, k, v, o, d_o, lse, position_ids, n_tokens, n_q_heads, n_kv_heads,
-                           head_dim, scale, grad_dtype == SP_DTYPE_F32, dq, dk, dv, strides, ws,
-                           stream) == hipSuccess ? SP_OK : SP_E_HIP;
+    return attn_bwd_checked(q, q_stride, k, v, kv_stride, o, o_stride, d_o, do_stride, lse,
+                            position_ids, n_tokens, n_q_heads, n_kv_heads, head_dim,
+                            softmax_scale, grad_dtype, dq, dq_stride, dk, dk_stride, dv, dv_stride,
+                            workspace, workspace_bytes, false, stream);
 }
 
 sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o, const void *d_o,
@@ -246,6 +315,17 @@ sp_status sp_attn_bwd(const void *q, const void *k, const void *v, const void *o
     return sp_attn_bwd_strided(q, sq, k, v, skv, o, sq, d_o, sq, lse, position_ids, n_tokens,
                                n_q_heads, n_kv_heads, head_dim, softmax_scale, grad_dtype, dq, sq,
                                dk, skv, dv, skv, workspace, workspace_bytes, stream);
+}
+
+sp_status sp_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                              const void *d_o, const float *lse, const int64_t *position_ids,
+                              int64_t n_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                              float softmax_scale, int grad_dtype, void *dq, void *dk, void *dv,
+                              hipStream_t stream) {
+    const int64_t sq = (int64_t)n_q_heads * head_dim, skv = (int64_t)n_kv_heads * head_dim;
+    return attn_bwd_checked(q, sq, k, v, skv, o, sq, d_o, sq, lse, position_ids, n_tokens,
+                            n_q_heads, n_kv_heads, head_dim, softmax_scale, grad_dtype, dq, sq,
+                            dk, skv, dv, skv, nullptr, 0, true, stream);
 }
 
 size_t sp_linear_ce_workspace_bytes(int64_t vocab, int64_t chunk_tokens) {

@@ -54,7 +54,11 @@ struct AttnWorkspace {
     void *vt;          // fwd: V transposed, keys permuted within groups of 16 [hkv][d][Npad]
 };
 
-size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws);
+// Lays the workspace out from `base` (nullptr: sizes only) and returns its
+// size; with_vt = false leaves out the forward's transposed V (vt = nullptr),
+// which the backward does not use.
+size_t attn_workspace_layout(int64_t N, int hq, int hkv, int d, void *base, AttnWorkspace *ws,
+                             bool with_vt = true);
 
 // The dK/dV kernel reads query rows of one KV head straight from q and dO
 // when its g = hq/hkv query heads per token are a power of two dividing 32

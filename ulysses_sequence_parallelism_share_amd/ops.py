@@ -194,6 +194,40 @@ def sp_attn_bwd(q, k, v, o, d_o, lse, position_ids, softmax_scale: float = 0.0,
     return dq, dk, dv
 
 
+def sp_attn_bwd_noalloc(q, k, v, o, d_o, lse, position_ids, softmax_scale: float = 0.0,
+                        grad_dtype=torch.float32, dq=None, dk=None, dv=None):
+    """sp_attn_bwd with the library's fixed device scratch instead of a workspace
+    (the C call allocates nothing; pass dq, dk, dv to keep this wrapper from
+    allocating its outputs)."""
+    N, hq, d = q.shape
+    hkv = k.shape[1]
+    for t, name, shp in ((q, "q", None), (k, "k", (N, hkv, d)), (v, "v", (N, hkv, d)),
+                         (o, "o", (N, hq, d)), (d_o, "d_o", (N, hq, d))):
+        _need(t, name, _BF16, shp)
+    _need(lse, "lse", torch.float32, (hq, N))
+    _need(position_ids, "position_ids", torch.int64, (N,))
+    if grad_dtype == torch.float32:
+        code = _lib.SP_DTYPE_F32
+    elif grad_dtype == torch.bfloat16:
+        code = _lib.SP_DTYPE_BF16
+    else:
+        raise TypeError("grad_dtype must be torch.float32 or torch.bfloat16")
+    if dq is None:
+        dq = torch.empty((N, hq, d), dtype=grad_dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty((N, hkv, d), dtype=grad_dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty((N, hkv, d), dtype=grad_dtype, device=q.device)
+    _need(dq, "dq", grad_dtype, (N, hq, d))
+    _need(dk, "dk", grad_dtype, (N, hkv, d))
+    _need(dv, "dv", grad_dtype, (N, hkv, d))
+    _lib.check("sp_attn_bwd_noalloc", _lib.call(
+        "sp_attn_bwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse),
+        _ptr(position_ids), N, hq, hkv, d, float(softmax_scale), code, _ptr(dq), _ptr(dk),
+        _ptr(dv), _stream()))
+    return dq, dk, dv
+
+
 def _need_rows(t: torch.Tensor, name: str, dtype, shape) -> int:
     """A [N][h][d] view whose heads and elements are packed (strides (s, d, 1));
     returns the token stride s."""
