@@ -45,6 +45,9 @@ def parse():
                     help="timed round trips of the relayout-bound workload and of the K/V exchange (0: skip)")
     ap.add_argument("--cpu-tokens", type=int, default=20480,
                     help="tokens of the oracle's CPU-baseline sample (0: skip)")
+    ap.add_argument("--other-configs", type=int, default=3,
+                    help="timed fwd+bwd repetitions on the 32768- and 131072-token rank shares "
+                         "(0: skip)")
     ap.add_argument("--lce-steps", type=int, default=3,
                     help="timed calls of the fused cross-entropy workload (0: skip)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
@@ -68,16 +71,51 @@ def to_dev_bf16(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
 
-def cpu_baseline(w, tokens):
-    """The oracle's fwd+bwd on the first `tokens` tokens of the workload's first packed
-    sample (one causal sample, the workload's heads and head_dim), timed on the host."""
-    from oracle import ref
-    from synth import gen
+def _host_info():
+    """Host cores, affinity, CPU model and BLAS threads of the process."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+        blas = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
     except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        blas = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu_count": os.cpu_count(), "affinity": aff, "cpu_model": model,
+            "blas_threads": int(blas)}
+
+
+def _gate(name, got, ref_, rel_tol=5e-3, abs_tol=2e-2):
+    got = np.asarray(got, np.float64)
+    d = got - ref_
+    rel = float(np.linalg.norm(d) / np.linalg.norm(ref_))
+    mx = float(np.abs(d).max())
+    return {"relL2": rel, "maxabs": mx, "pass": bool(np.isfinite(got).all() and rel <= rel_tol
+                                                     and mx <= abs_tol)}
+
+
+def cpu_baseline(w, tokens, dev):
+    """The oracle (fp64 numpy) timed on the host on a bounded sample of the workload,
+    and the in-job parity check on that sample.
+
+    Attention: the first `tokens` tokens of the workload's first packed sample (one
+    causal sample, the workload's heads and head_dim), fwd + bwd; the GPU path runs on
+    the same inputs (fp32 gradients) and every output element is compared with the
+    oracle's under the gates (relative L2 <= 5e-3, max abs <= 2e-2).  Also timed, each
+    checked against the GPU: the seq->head relayout of a slice of the relayout-bound
+    buffer (bit-exact) and the token-weighted loss of the long-sequence workload."""
+    import torch
+    from oracle import ref
+    from synth import configs, gen
+    from ulysses_sequence_parallelism_share_amd import ops
+    host = _host_info()
     L = min(tokens, w.lengths()[0])
     q = gen.normal_bf16((w.cfg, 1), (L, w.hq, w.head_dim))
     k = gen.normal_bf16((w.cfg, 2), (L, w.hkv, w.head_dim))
@@ -85,16 +123,93 @@ def cpu_baseline(w, tokens):
     do = gen.normal_bf16((w.cfg, 4), (L, w.hq, w.head_dim))
     pos = np.arange(L, dtype=np.int64)
     t0 = time.perf_counter()
-    ref.attn_fwd(q, k, v, pos)
-    ref.attn_bwd(q, k, v, do, pos)
-    dt = time.perf_counter() - t0
+    o_r, lse_r = ref.attn_fwd(q, k, v, pos)
+    t1 = time.perf_counter()
+    dq_r, dk_r, dv_r = ref.attn_bwd(q, k, v, do, pos)
+    t2 = time.perf_counter()
+    # the GPU path on the same sample
+    qd, kd, vd, dod = (to_dev_bf16(a, dev) for a in (q, k, v, do))
+    posd = torch.from_numpy(pos).to(dev)
+    o, lse = ops.sp_attn_fwd(qd, kd, vd, posd)
+    dq, dk, dv = ops.sp_attn_bwd(qd, kd, vd, o, dod, lse, posd)
+    f64 = lambda t: (ref.bf16_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+                     if t.dtype == torch.bfloat16 else t.double().cpu().numpy())
+    parity = {"sample": f"first {L} tokens of the workload's first packed sample, all heads",
+              "O": _gate("O", f64(o), o_r), "dQ": _gate("dQ", f64(dq), dq_r),
+              "dK": _gate("dK", f64(dk), dk_r), "dV": _gate("dV", f64(dv), dv_r),
+              "lse_maxabs": float(np.abs(f64(lse) - lse_r).max())}
+    del qd, kd, vd, dod, o, lse, dq, dk, dv
+    # relayout: a slice of the relayout-bound buffer (P=8, 1024 tokens per rank)
+    w4 = configs.WORKLOADS[4]
+    xs = gen.normal_bf16((w4.cfg, 1), (w4.sp_size, 1024, w4.relayout_groups, w4.relayout_heads,
+                                       w4.head_dim))
+    t3 = time.perf_counter()
+    h_r = ref.seq_to_head(xs)
+    t4 = time.perf_counter()
+    h_g = ops.ulysses_seq_to_head(to_dev_bf16(xs, dev))
+    parity["relayout_bit_exact"] = bool(np.array_equal(
+        h_g.view(torch.int16).cpu().numpy().view(np.uint16), h_r))
+    # token-weighted loss of the long-sequence workload (N=131072 over 8 ranks, 10 % prompt)
+    li = configs.loss_inputs(configs.WORKLOADS[3])
+    t5 = time.perf_counter()
+    l_r, _, good_r, _ = ref.weighted_loss(li["token_loss"], li["shift_labels"])
+    t6 = time.perf_counter()
+    l_g, _, good_g, _ = ops.sp_weighted_loss(torch.from_numpy(li["token_loss"]).to(dev),
+                                              torch.from_numpy(li["shift_labels"]).to(dev))
+    parity["loss_counts_exact"] = bool(np.array_equal(good_g.cpu().numpy(), good_r))
+    parity["loss_relerr"] = abs(float(l_g.cpu()[0]) - l_r) / abs(l_r)
+    parity["pass"] = bool(all(parity[n]["pass"] for n in ("O", "dQ", "dK", "dV"))
+                          and parity["lse_maxabs"] <= 1e-3 and parity["relayout_bit_exact"]
+                          and parity["loss_counts_exact"] and parity["loss_relerr"] <= 1e-5)
     A = L * (L + 1) // 2
     flops = 14.0 * w.head_dim * A * w.hq
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
+    dt = t2 - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host["blas_threads"],
+            "kind": "oracle", "seconds": dt,
             "sample": f"fp64 oracle attn_fwd+attn_bwd on one causal sample of {L} tokens "
                       f"(the first {L} tokens of the workload's first packed sample), "
-                      f"hq={w.hq}, hkv={w.hkv}, d={w.head_dim}; {flops:.3e} algorithmic FLOP"}
+                      f"hq={w.hq}, hkv={w.hkv}, d={w.head_dim}; {flops:.3e} algorithmic FLOP",
+            "host": host,
+            "phases_s": {"attn_fwd": t1 - t0, "attn_bwd": t2 - t1, "relayout": t4 - t3,
+                         "loss": t6 - t5},
+            "relayout_GB/s": 2 * xs.nbytes / (t4 - t3) / 1e9,
+            "relayout_sample": f"seq->head of [8][1024][3][32][128] bf16 ({xs.nbytes} bytes)",
+            "loss_sample": "token-weighted loss over 8 ranks x 16384 tokens"}, parity
+
+
+def attention_config(dev, cfg, reps):
+    """Attention fwd+bwd (bf16 gradients) on a rank-share workload without relayouts:
+    average ms per fwd+bwd pair of calls and TFLOP/s of 14 d A hq."""
+    import torch
+    from synth import configs
+    from ulysses_sequence_parallelism_share_amd import ops
+    w = configs.WORKLOADS[cfg]
+    inp = configs.rank_share_inputs(w)
+    q, k, v, do = (to_dev_bf16(inp[n], dev) for n in ("q", "k", "v", "do"))
+    pos = torch.from_numpy(inp["pos"]).to(dev)
+    N, hq, hkv, d = w.n_tokens, w.hq, w.hkv, w.head_dim
+    ws = ops.workspace(N, hq, hkv, d, dev)
+    o = torch.empty((N, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((hq, N), dtype=torch.float32, device=dev)
+    g = [torch.empty((N, h, d), dtype=torch.bfloat16, device=dev) for h in (hq, hkv, hkv)]
+
+    def one():
+        ops.sp_attn_fwd(q, k, v, pos, o=o, lse=lse, ws=ws)
+        ops.sp_attn_bwd(q, k, v, o, do, lse, pos, grad_dtype=torch.bfloat16, dq=g[0], dk=g[1],
+                        dv=g[2], ws=ws)
+
+    one()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        one()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flop = 14.0 * d * w.allowed_pairs() * hq
+    return {"workload": w.name, "sample_lengths": w.lengths(), "ms_fwd_bwd": ms,
+            "TFLOP/s": flop / ms / 1e9, "frac_mfma": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
 
 # ---------------------------------------------------------------------------
 # HBM traffic of the attention kernels, from rocprofv3 counters.
@@ -600,6 +715,14 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
 
+    cpu = parity = None
+    if args.cpu_tokens > 0:
+        # the oracle on a bounded sample, and the in-job parity check on it, before timing
+        t1 = time.time()
+        cpu, parity = cpu_baseline(w, args.cpu_tokens, dev)
+        log(f"[bench] cpu baseline and parity check done in {time.time() - t1:.1f}s "
+            f"(parity {'pass' if parity['pass'] else 'FAIL'})")
+
     relayout_bytes = 0
 
     def step():
@@ -726,11 +849,14 @@ def main():
         log(f"[bench] linear cross-entropy: {lce['ms_per_call']:.2f} ms/call "
             f"({time.time() - t1:.1f}s)")
 
-    cpu = None
-    if args.cpu_tokens > 0:
-        t1 = time.time()
-        cpu = cpu_baseline(w, args.cpu_tokens)
-        log(f"[bench] cpu baseline done in {time.time() - t1:.1f}s")
+    other = None
+    if args.other_configs > 0 and args.workload == 5:
+        other = {}
+        for cfg in (2, 3):
+            t1 = time.time()
+            other[str(cfg)] = attention_config(dev, cfg, args.other_configs)
+            log(f"[bench] config {cfg}: {other[str(cfg)]['TFLOP/s']:.0f} TFLOP/s "
+                f"({time.time() - t1:.1f}s)")
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
@@ -743,6 +869,8 @@ def main():
                    f"{P}) on 1 GPU; all-to-all emulated on device"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
+        "other_configs": other,
         "attention": attention,
         "relayout_step": relayout,
         "zero_copy_step": zero_copy,

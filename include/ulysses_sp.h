@@ -337,7 +337,7 @@ sp_status sp_linear_ce(const void *x, const void *w, const int64_t *labels, int6
  *   d_token_loss  [sp_size][n_tokens/sp_size]  fp32 (written; may be NULL):
  *                 d loss / d token_loss = 1/max(T,1) on valid tokens, else 0
  * Errors: SP_E_NOT_DIVISIBLE if n_tokens % sp_size; SP_E_SHAPE if sp_size < 1
- * or n_tokens < 0; SP_E_NULL; SP_E_ALIGN.  With n_tokens == 0 the outputs are
+ * or n_tokens is negative or at least 2^48; SP_E_NULL; SP_E_ALIGN.  With n_tokens == 0 the outputs are
  * loss 0, rank_loss NaN and good_tokens 0.
  */
 sp_status sp_weighted_loss(const float *token_loss, const int64_t *shift_labels, int sp_size,

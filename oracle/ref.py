@@ -502,3 +502,31 @@ def linear_cross_entropy(x, w, labels, g=None, ignore_index=IGNORE_INDEX):
     G[np.arange(len(labels)), idx] -= 1.0
     G *= (np.asarray(g, dtype=np.float64) * valid)[:, None]
     return token_loss, lse, G @ w, G.T @ x
+
+
+def linear_ce_vocab_rows(x, w, labels, g, vrows, ignore_index=IGNORE_INDEX, chunk=256):
+    """dw of linear_cross_entropy for selected vocabulary rows only:
+        dw_v = sum_t G_tv x_t,  G_tv = g_t (softmax_v(logit_t) - [v == labels_t])
+    over the valid tokens.  Every token's log-sum-exp comes from its full row of
+    logits (one pass over the vocabulary, tokens taken `chunk` at a time); only the
+    requested columns of G are formed.  Returns lse [N] and dw [R][K] (float64)."""
+    x, w = _as_f64(x), _as_f64(w)
+    labels = np.asarray(labels)
+    g = np.asarray(g, dtype=np.float64)
+    vrows = np.asarray(vrows, dtype=np.int64)
+    N = x.shape[0]
+    lse = np.zeros(N)
+    dw = np.zeros((vrows.size, x.shape[1]))
+    for t0 in range(0, N, chunk):
+        t1 = min(N, t0 + chunk)
+        logits = x[t0:t1] @ w.T
+        m = logits.max(axis=1, keepdims=True)
+        lse_c = (m + np.log(np.exp(logits - m).sum(axis=1, keepdims=True)))[:, 0]
+        lse[t0:t1] = lse_c
+        lab = labels[t0:t1]
+        valid = lab != ignore_index
+        G = np.exp(logits[:, vrows] - lse_c[:, None])
+        G -= (lab[:, None] == vrows[None, :])
+        G *= (g[t0:t1] * valid)[:, None]
+        dw += G.T @ x[t0:t1]
+    return lse, dw

@@ -99,6 +99,7 @@ def test_lce_llama2_vocab_full_oracle():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(600)
 def test_lce_llama3_lm_head_sampled():
     """4096 tokens, vocabulary 128256, hidden 4096 (the benchmark's shapes and chunk):
     losses, lse and dx rows of sampled tokens against the oracle token by token, and
@@ -122,3 +123,17 @@ def test_lce_llama3_lm_head_sampled():
     bound = 1.1 * 2.0 ** -7 * (inp["g"].astype(np.float64) @ np.abs(ref.bf16_to_f64(inp["x"])))
     say(f"  |sum_v dw_v| max={np.abs(col).max():.3e}, bound min={bound.min():.3e}")
     assert np.all(np.abs(col) <= bound)
+    # dw element by element on >= 256 vocabulary rows: the labels of sampled tokens (the
+    # one-hot term), both ends of the vocabulary, both sides of 256-row tile edges, random
+    labs = inp["labels"][inp["labels"] >= 0]
+    vrows = np.unique(np.concatenate([labs[:96], [0, 1, w.vocab - 2, w.vocab - 1],
+                                      np.arange(256, w.vocab, 256)[::40] - 1,
+                                      np.arange(256, w.vocab, 256)[::40],
+                                      rng.integers(0, w.vocab, 96)]))
+    assert vrows.size >= 256
+    say(f"  dw: {vrows.size} vocabulary rows, lse from one fp64 pass over all logits")
+    lse_all, dw_r = ref.linear_ce_vocab_rows(inp["x"], inp["w"], inp["labels"], inp["g"], vrows)
+    e3 = np.abs(lse - lse_all).max()
+    say(f"  lse (all tokens) maxabs={e3:.3e}")
+    assert e3 <= LOSS_ABS
+    gate("dw (sampled vocabulary rows)", dw[vrows], dw_r)

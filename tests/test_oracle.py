@@ -774,3 +774,17 @@ def test_lce_shift_invariance_and_ignored_tokens():
     lab_all = np.full_like(lab, -100)
     tla, _, dxa, dwa = ref.linear_cross_entropy(x, w, lab_all, g)
     assert np.all(tla == 0) and np.all(dxa == 0) and np.all(dwa == 0)
+
+
+def test_lce_vocab_rows_match_full():
+    """dw of selected vocabulary rows (and every token's lse) equal the full oracle's,
+    including label rows (the one-hot term), with token chunks that do not divide N."""
+    x, w, lab, g = _lce_case(7, N=11, K=6, V=13, ignore=(2, 5))
+    tl, lse, dx, dw = ref.linear_cross_entropy(x, w, lab, g)
+    rows = np.array(sorted({0, 12, int(lab[0]), int(lab[3]), 7}))
+    lse_s, dw_s = ref.linear_ce_vocab_rows(x, w, lab, g, rows, chunk=4)
+    np.testing.assert_allclose(lse_s, lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dw_s, dw[rows], rtol=1e-12, atol=1e-13)
+    _, dw_all = ref.linear_ce_vocab_rows(x, w, lab, g, np.arange(13), chunk=3)
+    np.testing.assert_allclose(dw_all, dw, rtol=1e-12, atol=1e-13)
+

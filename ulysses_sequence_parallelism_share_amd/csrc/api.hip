@@ -7,6 +7,7 @@
 // "Configuration"); masking comes from position_ids only.
 #include <math.h>
 
+#include <initializer_list>
 #include <mutex>
 
 #include "../../include/ulysses_sp.h"
@@ -18,6 +19,18 @@ inline bool misaligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a -
 
 constexpr int64_t kMaxRows = (int64_t)1 << 30;  // token and virtual-row indices stay in int32
 
+// a0 * a1 * ... < lim, for non-negative factors, without overflow (the
+// running product stays below lim < 2^63 before each multiply, so it fits
+// in 128 bits)
+inline bool prod_below(std::initializer_list<int64_t> factors, int64_t lim) {
+    __int128 p = 1;
+    for (int64_t f : factors) {
+        p *= f;
+        if (p >= lim) return false;
+    }
+    return true;
+}
+
 sp_status check_relayout(const void *src, const void *dst, int P, int64_t N, int G, int H, int d,
                          int rank) {
     if (P < 1 || N < 0 || G < 1 || H < 1 || d < 1) return SP_E_SHAPE;
@@ -25,7 +38,8 @@ sp_status check_relayout(const void *src, const void *dst, int P, int64_t N, int
     if (rank < -1 || rank >= P) return SP_E_RANK;
     const int64_t piece = (int64_t)(H / P) * d;
     if (piece % 8 != 0) return SP_E_SHAPE;
-    if (N >= kMaxRows || (int64_t)G * H * d / 8 >= ((int64_t)1 << 24)) return SP_E_SHAPE;
+    // a token's G*H*d/8 16-byte vectors are indexed in 24 bits
+    if (N >= kMaxRows || !prod_below({G, H, d}, (int64_t)1 << 27)) return SP_E_SHAPE;
     if (N == 0) return SP_OK;
     if (src == nullptr || dst == nullptr) return SP_E_NULL;
     if (misaligned(src, 16) || misaligned(dst, 16)) return SP_E_ALIGN;
@@ -41,9 +55,9 @@ sp_status check_kv_relayout(const void *src, const void *dst, int P, int64_t N, 
     if (rank < -1 || rank >= P) return SP_E_RANK;
     if (d % 8 != 0) return SP_E_SHAPE;
     const int64_t hl = H >= P ? H / P : 1;
-    if (N * hl * (d / 8) >= ((int64_t)1 << 31) || N * H * (d / 8) >= ((int64_t)1 << 31) ||
-        (N / P) * G * H * (d / 8) >= ((int64_t)1 << 31) ||
-        (int64_t)P * G > 65535)
+    const int64_t lim = (int64_t)1 << 31;   // 16-byte chunk indices in 31 bits
+    if (!prod_below({N, hl, d / 8}, lim) || !prod_below({N, H, d / 8}, lim) ||
+        !prod_below({N / P, G, H, d / 8}, lim) || (int64_t)P * G > 65535)
         return SP_E_SHAPE;
     if (N == 0) return SP_OK;
     if (src == nullptr || dst == nullptr) return SP_E_NULL;
@@ -55,7 +69,7 @@ sp_status check_attn_shape(int64_t N, int hq, int hkv, int d, float scale) {
     if (N < 0 || hq < 1 || hkv < 1) return SP_E_SHAPE;
     if (d != 64 && d != 128) return SP_E_SHAPE;
     if (hq % hkv != 0) return SP_E_NOT_DIVISIBLE;
-    if (N * (int64_t)hq >= kMaxRows) return SP_E_SHAPE;
+    if (!prod_below({N, hq}, kMaxRows)) return SP_E_SHAPE;
     // Tile rows are addressed by 32-bit byte offsets from the tile base; the
     // longest span is the forward's V^T tile: head_dim rows of the transposed
     // copy, (n_tokens rounded up to 64) keys each.
@@ -76,6 +90,10 @@ inline bool bad_stride(int64_t stride, int heads, int d) {
 // the tile base: 255 * v_pad * 2 + 127 must stay below 2^32, which holds for
 // v_pad <= 8421376 (a multiple of 256), so the vocabulary is limited to that.
 constexpr int64_t kMaxLceVocab = 8421376;
+
+// The loss kernels index tokens with 64-bit integers; the grid arithmetic
+// adds a workgroup's worth to the count, so counts stay below 2^48.
+constexpr int64_t kMaxLossTokens = (int64_t)1 << 48;
 
 inline int64_t pad64(int64_t x) { return (x + 63) / 64 * 64; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -367,7 +385,7 @@ sp_status sp_linear_ce(const void *x, const void *w, const int64_t *labels, int6
 sp_status sp_weighted_loss(const float *token_loss, const int64_t *shift_labels, int sp_size,
                            int64_t n_tokens, int64_t ignore_index, float *loss, float *rank_loss,
                            int64_t *good_tokens, float *d_token_loss, hipStream_t stream) {
-    if (sp_size < 1 || n_tokens < 0) return SP_E_SHAPE;
+    if (sp_size < 1 || n_tokens < 0 || n_tokens >= kMaxLossTokens) return SP_E_SHAPE;
     if (n_tokens % sp_size != 0) return SP_E_NOT_DIVISIBLE;
     if (!loss || !rank_loss || !good_tokens) return SP_E_NULL;
     if (n_tokens > 0 && (!token_loss || !shift_labels)) return SP_E_NULL;

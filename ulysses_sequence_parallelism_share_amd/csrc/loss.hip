@@ -10,7 +10,11 @@
 // is the number of valid tokens over all ranks.  On one GPU the all_gather
 // of the per-rank (loss, count) pairs becomes a read of a [P] buffer.
 //
-// k_loss_rank: one workgroup per rank, fp64 sum and int64 count.
+// k_loss_rank: one workgroup of 1024 threads per rank, fp64 sum and int64
+// count; each thread keeps 8 independent loads of labels and losses in
+// flight (the pass is bound by load latency, not bandwidth), and the
+// per-thread sums meet in a fixed reduction tree, so the result is
+// deterministic.
 // k_loss_finish: combines the P pairs and writes the per-token gradient
 // 1/max(T,1) on valid tokens.
 #include "common.h"
@@ -19,24 +23,36 @@
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRankThreads = 1024;
+constexpr int kUnroll = 8;
 
-__global__ __launch_bounds__(kThreads) void k_loss_rank(const float *__restrict__ token_loss,
-                                                        const int64_t *__restrict__ labels,
-                                                        int64_t T, int64_t ignore_index,
-                                                        float *__restrict__ rank_loss,
-                                                        int64_t *__restrict__ good) {
-    __shared__ double ssum[kThreads / 64];
-    __shared__ long long scnt[kThreads / 64];
+__global__ __launch_bounds__(kRankThreads) void k_loss_rank(const float *__restrict__ token_loss,
+                                                            const int64_t *__restrict__ labels,
+                                                            int64_t T, int64_t ignore_index,
+                                                            float *__restrict__ rank_loss,
+                                                            int64_t *__restrict__ good) {
+    __shared__ double ssum[kRankThreads / 64];
+    __shared__ long long scnt[kRankThreads / 64];
     const int r = blockIdx.x;
     const float *tl = token_loss + (size_t)r * T;
     const int64_t *lb = labels + (size_t)r * T;
     double sum = 0.0;
     long long cnt = 0;
-    for (int64_t i = threadIdx.x; i < T; i += kThreads) {
-        if (lb[i] != ignore_index) {
-            sum += (double)tl[i];
-            ++cnt;
+    for (int64_t base = threadIdx.x; base < T; base += (int64_t)kRankThreads * kUnroll) {
+        int64_t lv[kUnroll];
+        float tv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t i = base + (int64_t)u * kRankThreads;
+            lv[u] = i < T ? lb[i] : ignore_index;
+            tv[u] = i < T ? tl[i] : 0.f;
         }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (lv[u] != ignore_index) {
+                sum += (double)tv[u];
+                ++cnt;
+            }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
@@ -52,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void k_loss_rank(const float *__restrict_
     if (threadIdx.x == 0) {
         double s = 0.0;
         long long c = 0;
-        for (int w = 0; w < kThreads / 64; ++w) {
+        for (int w = 0; w < kRankThreads / 64; ++w) {
             s += ssum[w];
             c += scnt[w];
         }
@@ -92,7 +108,7 @@ hipError_t launch_weighted_loss(const float *token_loss, const int64_t *labels, 
     const int64_t T = N / P;
     {
         KernelTimer timer("loss_rank", stream);
-        hipLaunchKernelGGL(k_loss_rank, dim3((unsigned)P), dim3(kThreads), 0, stream, token_loss,
+        hipLaunchKernelGGL(k_loss_rank, dim3((unsigned)P), dim3(kRankThreads), 0, stream, token_loss,
                        labels, T, ignore_index, rank_loss, good);
     }
     hipError_t e = hipGetLastError();
