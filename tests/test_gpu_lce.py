@@ -129,7 +129,7 @@ def test_lce_llama3_lm_head_sampled():
     vrows = np.unique(np.concatenate([labs[:96], [0, 1, w.vocab - 2, w.vocab - 1],
                                       np.arange(256, w.vocab, 256)[::40] - 1,
                                       np.arange(256, w.vocab, 256)[::40],
-                                      rng.integers(0, w.vocab, 96)]))
+                                      rng.integers(0, w.vocab, 160)]))
     assert vrows.size >= 256
     say(f"  dw: {vrows.size} vocabulary rows, lse from one fp64 pass over all logits")
     lse_all, dw_r = ref.linear_ce_vocab_rows(inp["x"], inp["w"], inp["labels"], inp["g"], vrows)
