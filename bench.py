@@ -268,9 +268,9 @@ def summarize_traffic(fetch_csv, write_csv):
            "# (N=524288, hq=4, hkv=1, d=128, 4 packed samples)",
            "# commands (GPU, from /tmp with TMPDIR=/tmp; REPO = the repository root):",
            "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d REPO/gpurun_out/pmc_fetch -o run "
-           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0",
+           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0 --other-configs 0",
            "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d REPO/gpurun_out/pmc_write -o run "
-           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0",
+           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0 --other-configs 0",
            "#   python3 REPO/bench.py --summarize-traffic "
            "REPO/gpurun_out/pmc_fetch/run_counter_collection.csv "
            "REPO/gpurun_out/pmc_write/run_counter_collection.csv",
@@ -349,7 +349,8 @@ def summarize_counters(csv_path):
            "# d=128, 4 packed samples)",
            "# commands (GPU, from /tmp with TMPDIR=/tmp; REPO = the repository root):",
            f"#   rocprofv3 --pmc {COUNTER_PASS} --output-format csv -d REPO/gpurun_out/pmc_sq -o run "
-           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0 --lce-steps 1",
+           "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0 --other-configs 0 "
+           "--lce-steps 1",
            "#   python3 REPO/bench.py --summarize-counters REPO/gpurun_out/pmc_sq/run_counter_collection.csv",
            "# mfma_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (executed_flop: 4/8/6 d A hq for fwd/dK,dV/dQ);",
            "# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES /",
