@@ -170,6 +170,7 @@ def cpu_baseline(w, tokens, dev):
                       f"(the first {L} tokens of the workload's first packed sample), "
                       f"hq={w.hq}, hkv={w.hkv}, d={w.head_dim}; {flops:.3e} algorithmic FLOP",
             "host": host,
+            "extrapolated_full_workload_s": 14.0 * w.head_dim * w.allowed_pairs() * w.hq / (flops / dt),
             "phases_s": {"attn_fwd": t1 - t0, "attn_bwd": t2 - t1, "relayout": t4 - t3,
                          "loss": t6 - t5},
             "relayout_GB/s": 2 * xs.nbytes / (t4 - t3) / 1e9,
