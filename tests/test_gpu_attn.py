@@ -66,10 +66,13 @@ def test_attention_parity(name, N, hq, hkv, d, lens, scale):
     # deterministic: a second call gives identical bits
     dq2, dk2, dv2 = ops.sp_attn_bwd(qd, kd, vd, o, dod, lse, posd, softmax_scale=scale)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
-    # bf16 gradient outputs: same values rounded (reported; gated on relative L2 only)
+    # bf16 gradient outputs: the same fp32 accumulators rounded once to nearest-even,
+    # i.e. exactly torch's conversion of the fp32 outputs
     bq, bk, bv = ops.sp_attn_bwd(qd, kd, vd, o, dod, lse, posd, softmax_scale=scale,
                                  grad_dtype=torch.bfloat16)
-    for nm, g, r in (("dQ bf16", bq, dq_r), ("dK bf16", bk, dk_r), ("dV bf16", bv, dv_r)):
+    for nm, g, f, r in (("dQ bf16", bq, dq, dq_r), ("dK bf16", bk, dk, dk_r),
+                        ("dV bf16", bv, dv, dv_r)):
+        assert torch.equal(g.view(torch.int16), f.to(torch.bfloat16).view(torch.int16)), nm
         rel, mx = errors(f64_of(g), r)
         say(f"  {nm}: relL2={rel} maxabs={mx:.3e}")
         assert (rel is None and mx <= 1e-5) or (rel is not None and rel <= 1e-2)
@@ -342,6 +345,11 @@ def test_500k_share_through_relayout_deep():
     doh = ops.ulysses_seq_to_head(do_seq, rank=0)[0]
     o, lse = ops.sp_attn_fwd(qh, kvh[0], kvh[1], posd)
     dq, dk, dv = ops.sp_attn_bwd(qh, kvh[0], kvh[1], o, doh, lse, posd)
+    # the benchmark's bf16 gradients are these fp32 gradients rounded to nearest-even
+    for g32, g16 in zip((dq, dk, dv), ops.sp_attn_bwd(qh, kvh[0], kvh[1], o, doh, lse, posd,
+                                                      grad_dtype=torch.bfloat16)):
+        assert torch.equal(g16.view(torch.int16), g32.to(torch.bfloat16).view(torch.int16))
+    torch.cuda.empty_cache()
     o_seq = ops.ulysses_head_to_seq(o[None], P, rank=0, out=torch.zeros_like(q_seq))
     q = ref.gather_share(inp["q_seq"], 0)[:, 0]
     k = ref.gather_share(inp["kv_seq"], 0, 0, 1)[:, 0]
