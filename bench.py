@@ -224,16 +224,18 @@ def attention_config(dev, cfg, reps):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_500k_share_hbm_traffic.txt")
 KERNEL_SYMBOL = {"attn_fwd": "k_attn_fwd", "attn_bwd_dkdv": "k_attn_bwd_dkdv",
                  "attn_bwd_dq": "k_attn_bwd_dq"}
-KERNEL_SOURCES = {"attn_fwd": "attn_fwd.hip", "attn_bwd_dkdv": "attn_bwd.hip",
-                  "attn_bwd_dq": "attn_bwd.hip"}
+KERNEL_SOURCES = {"attn_fwd": ("attn_fwd.hip",),
+                  "attn_bwd_dkdv": ("attn_bwd.hip", "attn_bwd_dkdv.inc"),
+                  "attn_bwd_dq": ("attn_bwd.hip", "attn_bwd_dq.inc")}
 
 
 def sources_hash(kernel):
     import hashlib
     csrc = os.path.join(ROOT, "ulysses_sequence_parallelism_share_amd", "csrc")
     h = hashlib.sha256()
-    for f in (os.path.join(csrc, KERNEL_SOURCES[kernel]), os.path.join(csrc, "common.h"),
-              os.path.join(csrc, "tile.h"), os.path.join(csrc, "launch.h"),
+    files = [os.path.join(csrc, n) for n in (*KERNEL_SOURCES[kernel], "common.h", "tile.h",
+                                             "launch.h")]
+    for f in (*files,
               os.path.join(ROOT, "ulysses_sequence_parallelism_share_amd", "build.py")):
         with open(f) as fh:
             text = fh.read()

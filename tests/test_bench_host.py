@@ -124,11 +124,26 @@ def test_load_traffic_checks_the_source_hash(tmp_path, monkeypatch):
     assert bench.load_traffic("attn_bwd_dkdv") is None
 
 
-def test_source_hash_ignores_comments_only():
-    h = bench.sources_hash("attn_bwd_dkdv")
-    assert h == bench.sources_hash("attn_bwd_dq")          # same source file
-    assert h != bench.sources_hash("attn_fwd")
-    assert len(h) == 16
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    import shutil
+    pkg = os.path.join(bench.ROOT, "ulysses_sequence_parallelism_share_amd")
+    copy = tmp_path / "ulysses_sequence_parallelism_share_amd"
+    shutil.copytree(os.path.join(pkg, "csrc"), copy / "csrc")
+    shutil.copy(os.path.join(pkg, "build.py"), copy / "build.py")
+    names = ("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq")
+    base = {n: bench.sources_hash(n) for n in names}
+    assert len(set(base.values())) == 3 and all(len(h) == 16 for h in base.values())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert {n: bench.sources_hash(n) for n in names} == base
+    # comments and layout: no change
+    body = copy / "csrc" / "attn_bwd_dq.inc"
+    body.write_text("// a comment\n" + body.read_text().replace(";", ";  /* x */"))
+    assert {n: bench.sources_hash(n) for n in names} == base
+    # code: the kernels built from that file change, the others do not
+    body.write_text(body.read_text() + "\nint extra_symbol;\n")
+    now = {n: bench.sources_hash(n) for n in names}
+    assert now["attn_bwd_dq"] != base["attn_bwd_dq"]
+    assert now["attn_bwd_dkdv"] == base["attn_bwd_dkdv"] and now["attn_fwd"] == base["attn_fwd"]
 
 
 def test_trace_summary_table(tmp_path):

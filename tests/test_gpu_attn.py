@@ -417,3 +417,32 @@ def test_head_dim_64_gqa_share_deep(w):
     assert rows.size >= 4096 and cols.size >= 4096
     dk_g, dv_g = _deep_check(q, k, v, do, pos, o, lse, dq, dk, dv, [(0, N)], rows, cols)
     _sum_invariants(do, lens, dk_g, dv_g)
+
+
+def test_fused_and_separate_backward_launches_agree():
+    """Small grids run the dK/dV and dQ work in one launch, large ones in two.  A
+    65536-token sequence (512 dK/dV workgroups: one launch) and the same sequence
+    followed by a 192-token sample (514: two launches) give, on the shared sample,
+    the same bits: the block-diagonal mask keeps the extra sample out of it."""
+    import torch
+    ops = _ops()
+    hq, hkv, d, N1, extra = 4, 1, 128, 65536, 192
+    N2 = N1 + extra
+    say(f"fused (N={N1}) against separate (N={N2}) backward launches")
+    q, k, v, do = _inputs(61, N2, hq, hkv, d)
+    outs = []
+    for n, lens in ((N1, [N1]), (N2, [N1, extra])):
+        qd, kd, vd, dod = (to_dev_bf16(np.ascontiguousarray(a[:n])) for a in (q, k, v, do))
+        posd = to_dev(gen.position_ids_from_lengths(lens))
+        ops.sp_timing_enable(True)
+        ops.sp_timing_collect()
+        o, lse = ops.sp_attn_fwd(qd, kd, vd, posd)
+        dq, dk, dv = ops.sp_attn_bwd(qd, kd, vd, o, dod, lse, posd)
+        torch.cuda.synchronize()
+        names = set(ops.sp_timing_collect())
+        ops.sp_timing_enable(False)
+        outs.append((o[:N1], lse[:, :N1], dq[:N1], dk[:N1], dv[:N1], names))
+    assert "attn_bwd_fused" in outs[0][5] and "attn_bwd_dkdv" not in outs[0][5]
+    assert "attn_bwd_dkdv" in outs[1][5] and "attn_bwd_fused" not in outs[1][5]
+    for a, b in zip(outs[0][:5], outs[1][:5]):
+        assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
