@@ -355,16 +355,28 @@ def summarize_counters(csv_path):
            "-- python3 REPO/bench.py --steps 1 --warmup 0 --relayout-reps 1 --cpu-tokens 0 --other-configs 0 "
            "--lce-steps 1",
            "#   python3 REPO/bench.py --summarize-counters REPO/gpurun_out/pmc_sq/run_counter_collection.csv",
-           "# mfma_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (executed_flop: 4/8/6 d A hq for fwd/dK,dV/dQ);",
+           "# mfma_flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (executed_flop: 4/8/6 d A hq for fwd/dK,dV/dQ;",
+           "# 2 n V K for each cross-entropy product, 4096 x 128256 x 4096, the bench's --lce-steps call);",
            "# clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES /",
            "# (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), the share of SIMD-cycles with the matrix unit busy at",
            "# the clock the kernel ran at; tflops_at_clock_peak = 1024 FLOP x 1024 SIMDs x clock;",
            "# lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. Averages over the dispatches."]
-    for kernel, sym in KERNEL_SYMBOL.items():
-        pat = re.compile(r"(^|[\s:\d])" + sym + r"([<(]|I[LZN])")
-        rows = [e for e in disp.values() if pat.search(e["name"])]
+    # the fused cross-entropy's three products on the Llama-3-8B LM head (one call)
+    lw = configs.LCE_WORKLOADS[13]
+    gemm_flop = 2 * lw.n_tokens * lw.vocab * lw.hidden
+    kinds = [(k, s, None) for k, s in KERNEL_SYMBOL.items()] + [
+        ("lce_gemm_logits", "k_gemm<true, true,", gemm_flop),
+        ("lce_gemm_dx", "k_gemm<true, false,", gemm_flop),
+        ("lce_gemm_dw", "k_gemm<false, false,", gemm_flop)]
+    for kernel, sym, fixed_flop in kinds:
+        if fixed_flop is None:
+            pat = re.compile(r"(^|[\s:\d])" + sym + r"([<(]|I[LZN])")
+            rows = [e for e in disp.values() if pat.search(e["name"])]
+        else:
+            rows = [e for e in disp.values() if sym in e["name"]]
         if not rows:
             continue
+        executed[kernel] = executed.get(kernel, fixed_flop)
         n = len(rows)
         avg = lambda f: sum(f(e) for e in rows) / n
         ms = avg(lambda e: e["ns"]) / 1e6
