@@ -11,7 +11,7 @@ from oracle import ref
 from synth import configs, gen
 
 import oracle_par
-from helpers import LSE_ABS, bits_of, errors, f64_of, gate, say, to_dev, to_dev_bf16
+from helpers import LSE_ABS, MAX_ABS, bits_of, errors, f64_of, gate, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,11 @@ CASES = [  # name, N, hq, hkv, d, sample lengths, softmax_scale (0 = 1/sqrt(d))
     ("custom-scale", 400, 4, 1, 128, [250, 150], 0.05),
     ("long-tile-spanning", 2100, 4, 1, 64, [2100], 0.0),
     ("gqa3-two-kv-gathered-4k", 4096, 6, 2, 128, [1500, 1, 2595], 0.0),
+    # wide groups: 16 and 32 query heads per KV head (read in place, a 32-row block
+    # spans 2 or 1 tokens), and 5 (gathered rows)
+    ("gqa16-d64", 150, 16, 1, 64, [100, 50], 0.0),
+    ("gqa32", 70, 32, 1, 128, [70], 0.0),
+    ("gqa5-gathered", 333, 10, 2, 128, [200, 133], 0.0),
 ]
 
 
@@ -61,8 +66,13 @@ def test_attention_parity(name, N, hq, hkv, d, lens, scale):
     dq, dk, dv = ops.sp_attn_bwd(qd, kd, vd, o, dod, lse, posd, softmax_scale=scale)
     dq_r, dk_r, dv_r = ref.attn_bwd(q, k, v, do, pos, softmax_scale=scale or None)
     gate("dQ", f64_of(dq), dq_r)
-    gate("dK", f64_of(dk), dk_r)
-    gate("dV", f64_of(dv), dv_r)
+    # dK and dV sum over the query heads of a KV head: with 16 or more of them the
+    # bf16 rounding of P and dS alone exceeds the absolute 2e-2 (a CPU emulation of
+    # those roundings gives 2.1e-2 on the 16-head case), so those cases bound max abs
+    # by 1 % of the largest reference value instead; relative L2 stays 5e-3
+    wide = hq // hkv >= 16
+    for nm, got, r in (("dK", dk, dk_r), ("dV", dv, dv_r)):
+        gate(nm, f64_of(got), r, abs_tol=max(MAX_ABS, 0.01 * np.abs(r).max()) if wide else MAX_ABS)
     # deterministic: a second call gives identical bits
     dq2, dk2, dv2 = ops.sp_attn_bwd(qd, kd, vd, o, dod, lse, posd, softmax_scale=scale)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
