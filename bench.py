@@ -781,29 +781,57 @@ def main():
 
     per_step = {k: v["total_ms"] / args.steps for k, v in kt.items()}
     fwd_ms = kt["attn_fwd"]["avg_ms"]
-    dkdv_ms = kt["attn_bwd_dkdv"]["avg_ms"]
-    dq_ms = kt["attn_bwd_dq"]["avg_ms"]
+    # small grids run the backward as one fused launch (attn_bwd_fused)
+    fused = "attn_bwd_fused" in kt
+    dkdv_ms = None if fused else kt["attn_bwd_dkdv"]["avg_ms"]
+    dq_ms = None if fused else kt["attn_bwd_dq"]["avg_ms"]
+    bwd_ms = kt["attn_bwd_fused"]["avg_ms"] if fused else dkdv_ms + dq_ms
     attn_kernel_ms = sum(per_step.get(n, 0.0) for n in
                          ("segment_chunks", "segment_scan", "gather_rows", "attn_fwd_v_transpose",
-                          "attn_fwd", "bwd_rowstats", "attn_bwd_dkdv", "attn_bwd_dq"))
-    algo = {"attn_fwd": fwd_flop, "attn_bwd_dkdv": 0.8 * bwd_flop, "attn_bwd_dq": 0.2 * bwd_flop}
+                          "attn_fwd", "bwd_rowstats", "attn_bwd_dkdv", "attn_bwd_dq",
+                          "attn_bwd_fused"))
+    # algorithmic FLOP per launch (credited: 4 d A hq forward, 10 d A hq backward, of
+    # which 8 in the dK/dV kernel and 2 in dQ, whose S and dP recomputes are extra)
+    algo = ({"attn_fwd": fwd_flop, "attn_bwd_fused": bwd_flop} if fused else
+            {"attn_fwd": fwd_flop, "attn_bwd_dkdv": 0.8 * bwd_flop, "attn_bwd_dq": 0.2 * bwd_flop})
+    executed = {"attn_fwd": fwd_flop, "attn_bwd_dkdv": 0.8 * bwd_flop, "attn_bwd_dq": 0.6 * bwd_flop,
+                "attn_bwd_fused": 1.4 * bwd_flop}
     dom = max(algo, key=lambda n: kt[n]["avg_ms"])
     dom_tflops = algo[dom] / kt[dom]["avg_ms"] / 1e9
     roofline = {"kernel": dom, "bound": "mfma", "achieved": dom_tflops, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dom_tflops / PEAK_BF16_TFLOPS,
-                "traffic": load_traffic(dom) if args.workload == 5 else None,
+                "traffic": load_traffic(dom) if args.workload == 5 and dom in KERNEL_SOURCES else None,
                 "avg_ms": kt[dom]["avg_ms"], "algorithmic_flop_per_launch": algo[dom]}
     value = (fwd_flop + bwd_flop) / ms_per_step / 1e9
     attention = {
         "fwd_flop": fwd_flop, "bwd_flop": bwd_flop,
         "attn_fwd_ms": fwd_ms, "attn_bwd_dkdv_ms": dkdv_ms, "attn_bwd_dq_ms": dq_ms,
+        "attn_bwd_ms": bwd_ms, "bwd_fused_launch": fused,
         "fwd_kernel_tflops": fwd_flop / fwd_ms / 1e9,
-        "bwd_kernels_tflops": bwd_flop / (dkdv_ms + dq_ms) / 1e9,
+        "bwd_kernels_tflops": bwd_flop / bwd_ms / 1e9,
         "attention_calls_ms": attn_kernel_ms,
         "tflops_attention_kernels": (fwd_flop + bwd_flop) / attn_kernel_ms / 1e9,
         "frac_mfma_attention_kernels": (fwd_flop + bwd_flop) / attn_kernel_ms / 1e9 / PEAK_BF16_TFLOPS,
         "frac_mfma_step": value / PEAK_BF16_TFLOPS,
     }
+    # every attention kernel against its roofline: matrix kernels in TFLOP/s of
+    # their algorithmic (and executed) FLOP, the pre-passes in GB/s of the bytes
+    # they must move
+    Mpad = (N * (hq // hkv) + 63) // 64 * 64
+    hbm_bytes = {"attn_fwd_v_transpose": 2 * N * hkv * d * 2,
+                 "bwd_rowstats": N * hq * d * 2 * 2 + N * hq * 4 + 8 * hkv * Mpad}
+    kernel_rooflines = {}
+    for n, f in algo.items():
+        ms = kt[n]["avg_ms"]
+        kernel_rooflines[n] = {"bound": "mfma", "avg_ms": ms, "achieved": f / ms / 1e9,
+                               "executed_tflops": executed[n] / ms / 1e9, "unit": "TFLOP/s",
+                               "peak": PEAK_BF16_TFLOPS, "frac": f / ms / 1e9 / PEAK_BF16_TFLOPS}
+    for n, b in hbm_bytes.items():
+        if n in kt:
+            ms = kt[n]["avg_ms"]
+            kernel_rooflines[n] = {"bound": "hbm", "avg_ms": ms, "achieved": b / ms / 1e6,
+                                   "unit": "GB/s", "peak": PEAK_HBM_GBPS,
+                                   "frac": b / ms / 1e6 / PEAK_HBM_GBPS}
     zero_copy = None
     if relayout_in_step:
         # The same step with attention reading rank 0's heads in place from the
@@ -894,6 +922,7 @@ def main():
         "relayout_bound": relayout_bound_out,
         "kv_exchange": kv_ex,
         "kernels_ms_per_step": per_step,
+        "kernel_rooflines": kernel_rooflines,
     }
     print(json.dumps(line), flush=True)
 
